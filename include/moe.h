@@ -1,0 +1,135 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) top-k routed Mixture-of-Experts layer.
+ *
+ * The layer (forward pass only), per token t of x[T, d]:
+ *   L[t,:]  = W_r x[t] (+ b)                     router Linear, no bias in the pages
+ *   p[t,:]  = softmax(L[t,:])
+ *   S_t     = the k experts with the largest logits, largest first,
+ *             the lower expert index first among equal logits
+ *   w[t,j]  = p[t,S_j] / sum_i p[t,S_i]          renormalised top-k weights
+ *   out[t]  = sum_j w[t,j] * down_e( SiLU(gate_e x[t]) * up_e x[t] ),  e = S_j
+ * Sources: axonml-nn layers/moe.rs (docs.rs) -- Expert::forward,
+ * MoERouter::route, MoELayer::forward; "Mixtral MoE Block" (neurarch.com) --
+ * exported PyTorch _moe_forward and the Mixtral layer shapes.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are DEVICE pointers to row-major, contiguous arrays, each
+ *     aligned to 16 bytes. Weights use the nn.Linear [out, in] layout:
+ *       w_router [E, d], w_gate [E, ffn, d], w_up [E, ffn, d], w_down [E, d, ffn].
+ *   - dt is the storage dtype of x and of every weight (MOE_F32 or MOE_BF16);
+ *     logits, probabilities, gate weights and the router bias are always fp32,
+ *     expert indices int32. Arithmetic: fp32 accumulation everywhere.
+ *   - The caller owns every buffer. The library never allocates or frees
+ *     memory on these calls and keeps no state between them; any scratch it
+ *     needs comes from the caller's workspace (see moe_workspace_size).
+ *   - Each call checks its arguments on the host, enqueues its kernels on
+ *     `stream` (NULL = the default stream) and returns without waiting.
+ *     Outputs are valid once the caller has synchronised the stream.
+ *   - On any error nothing is enqueued and no output is written.
+ *   - T = 0 is valid: the call returns MOE_OK and launches nothing.
+ *   - Non-finite inputs are outside the contract (the page's sort cannot
+ *     order NaN); they are not detected on the device.
+ *   - Limits (MOE_UNSUPPORTED beyond them): E <= 256, k <= 16,
+ *     d % 16 == 0, ffn % 16 == 0, T * k < 2^31.
+ *   - Results are deterministic: no floating-point atomics are used, so two
+ *     calls on the same inputs give bit-identical outputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_INVALID_ARG = 1,          /* k<1, k>E, E<1, T<0, d<1, ffn<1, null or misaligned pointer */
+  MOE_UNSUPPORTED = 2,          /* beyond the limits above, or an unknown dtype */
+  MOE_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below moe_workspace_size(...) */
+  MOE_HIP_ERROR = 4             /* a kernel launch failed (hipGetLastError) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* moe_status_string(moe_status s);
+
+/* Bytes of device workspace that moe_forward and moe_expert_ffn need for this
+ * shape: routing results, per-expert offsets, the permutation, the hidden
+ * activations h [T*k, ffn] and expert outputs y [T*k, d] (in dt). Returns 0
+ * for invalid or unsupported shapes. Host-only; no device access. */
+size_t moe_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt);
+
+/* Router projection + softmax + top-k + renormalisation (one kernel).
+ * Computes logits L = x W_r^T (+ router_bias) in fp32, then the same routing
+ * as moe_route_logits on those logits.
+ *   x [T, d] (dt), w_router [E, d] (dt), router_bias [E] fp32 or NULL
+ *   (the pages' router has no bias; it exists for skewed-load workloads).
+ *   logits [T, E] fp32 or NULL; probs [T, E] fp32 or NULL;
+ *   topk_idx [T, k] int32, topk_w [T, k] fp32 (both required).
+ * Source: axonml-nn MoERouter::route; Mixtral _moe_forward (router, softmax,
+ * topk, division by the top-k sum). */
+moe_status moe_route(const void* x, const void* w_router, const float* router_bias,
+                     int T, int d, int E, int k, moe_dtype dt,
+                     float* logits, float* probs, int32_t* topk_idx, float* topk_w,
+                     hipStream_t stream);
+
+/* Routing from given fp32 logits [T, E]: softmax, top-k selection on the
+ * logits (descending; lowest index first among equal values, +0.0 == -0.0),
+ * and w[t,j] = p[S_j] / sum_i p[S_i]. Selection is a comparison of the fp32
+ * logits only, so it is bit-exact against any implementation fed the same
+ * logits. probs [T, E] may be NULL. topk_idx [T, k] int32 and topk_w [T, k]
+ * fp32 are required; slot 0 holds the largest logit.
+ * Source: axonml-nn MoERouter::route (stable descending sort, take k,
+ * renormalise). */
+moe_status moe_route_logits(const float* logits, int T, int E, int k,
+                            float* probs, int32_t* topk_idx, float* topk_w,
+                            hipStream_t stream);
+
+/* Expert histogram, exclusive prefix sum and stable permutation.
+ *   topk_idx [T, k] int32 with values in [0, E) (not checked on the device;
+ *   out-of-range indices are outside the contract).
+ *   counts [E]: assignments per expert; offsets [E+1]: offsets[0] = 0,
+ *   offsets[e+1] = offsets[e] + counts[e]; sorted_token [T*k]: the token of
+ *   each permuted row, experts in ascending order and, within an expert,
+ *   tokens in ascending order; inv_pos [T*k]: the row of assignment t*k+j.
+ * All integer; bit-exact. Source: axonml-nn MoELayer::forward (utilisation
+ * counts; per-expert token lists gathered in token order). */
+moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                       int32_t* inv_pos, hipStream_t stream);
+
+/* The expert half of the layer for a given routing: permute, per-expert
+ * SwiGLU h = SiLU(X W_g^T) * (X W_u^T), y = h W_d^T, and the weighted combine
+ * out[t] = sum_{j<k} topk_w[t,j] * y[row of (t,j)], summed in slot order in
+ * fp32. topk_idx [T, k] int32 holds k distinct experts per token; topk_w
+ * [T, k] fp32 is used as given (not renormalised here). out [T, d] in out_dt
+ * (MOE_F32 or MOE_BF16). ws: device workspace of at least
+ * moe_workspace_size(T, d, ffn, E, k, dt) bytes, 256-byte aligned.
+ * Source: axonml-nn Expert::forward and MoELayer::forward (gather, expert,
+ * weighted scatter-add); Mixtral _moe_forward. */
+moe_status moe_expert_ffn(const void* x, const int32_t* topk_idx, const float* topk_w,
+                          const void* w_gate, const void* w_up, const void* w_down,
+                          int T, int d, int ffn, int E, int k, moe_dtype dt,
+                          void* out, moe_dtype out_dt, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* The whole layer: moe_route, then moe_expert_ffn on its routing.
+ * router_bias, logits_out [T, E], probs_out [T, E] and counts_out [E] may be
+ * NULL. Everything else as above.
+ * Source: axonml-nn MoELayer::forward; Mixtral _moe_forward. */
+moe_status moe_forward(const void* x, const void* w_router, const void* w_gate,
+                       const void* w_up, const void* w_down, const float* router_bias,
+                       int T, int d, int ffn, int E, int k, moe_dtype dt,
+                       void* out, moe_dtype out_dt,
+                       float* logits_out, float* probs_out, int32_t* counts_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

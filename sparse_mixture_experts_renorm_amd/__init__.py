@@ -1,0 +1,9 @@
+"""MI355X (gfx950) top-k routed Mixture-of-Experts layer, forward pass.
+
+The computation lives in the HIP library libmoe_mi355x.so behind the C ABI
+of include/moe.h; this package only builds it and binds it with ctypes.
+"""
+from ._lib import (  # noqa: F401
+    MOE_BF16, MOE_F32, MoEError, declared_symbols, lib, moe_expert_ffn, moe_forward, moe_permute,
+    moe_route, moe_route_logits, moe_workspace_size, status_string, workspace,
+)

@@ -1,0 +1,220 @@
+"""ctypes binding of libmoe_mi355x.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls, checks the
+torch tensors it is given (device, dtype, shape, contiguity), allocates the
+outputs the caller did not pass, and hands raw device pointers plus the
+current HIP stream to the library. All arithmetic runs in the library's HIP
+kernels; there is no fallback: if the shared library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+
+MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_WORKSPACE_TOO_SMALL, MOE_HIP_ERROR = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def _p(name, restype, *argtypes):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is not built; run "
+                "`python -m sparse_mixture_experts_renorm_amd.build` (hipcc, gfx950)")
+        _lib = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        _p("moe_status_string", ctypes.c_char_p, i)
+        _p("moe_workspace_size", sz, i, i, i, i, i, i)
+        _p("moe_route", i, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp)
+        _p("moe_route_logits", i, vp, i, i, i, vp, vp, vp, vp)
+        _p("moe_permute", i, vp, i, i, i, vp, vp, vp, vp, vp)
+        _p("moe_expert_ffn", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, sz, vp)
+        _p("moe_forward", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp, vp, sz, vp)
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|size_t|moe_status)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, fn: str):
+    if status != MOE_OK:
+        raise MoEError(status, fn)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def moe_workspace_size(T: int, d: int, ffn: int, E: int, k: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().moe_workspace_size(T, d, ffn, E, k, dt))
+
+
+def workspace(T, d, ffn, E, k, dtype, device="cuda") -> torch.Tensor:
+    """A device byte buffer large enough for moe_forward / moe_expert_ffn."""
+    n = moe_workspace_size(T, d, ffn, E, k, dtype)
+    if n == 0:
+        raise ValueError("invalid or unsupported shape")
+    return torch.empty(n + 256, dtype=torch.uint8, device=device)
+
+
+def _ws_ptr(ws: torch.Tensor):
+    p = ws.data_ptr()
+    a = (p + 255) & ~255
+    return ctypes.c_void_p(a), ws.numel() - (a - p)
+
+
+def moe_route_logits(logits, k, probs=False, stream=None):
+    """Routing from fp32 logits [T,E]. Returns (topk_idx int32 [T,k],
+    topk_w f32 [T,k]) and probs f32 [T,E] as a third item if probs=True."""
+    _dev(logits)
+    assert logits.dtype == torch.float32 and logits.dim() == 2
+    T, E = logits.shape
+    dev = logits.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    p = torch.empty((T, E), dtype=torch.float32, device=dev) if probs else None
+    _check(lib().moe_route_logits(_ptr(logits), T, E, k, _ptr(p), _ptr(idx), _ptr(w), _stream(stream)),
+           "moe_route_logits")
+    return (idx, w, p) if probs else (idx, w)
+
+
+def moe_route(x, w_router, k, router_bias=None, want_logits=False, want_probs=False, stream=None):
+    """Fused router. Returns dict(topk_idx, topk_w[, logits][, probs])."""
+    _dev(x, w_router, router_bias)
+    T, d = x.shape
+    E = w_router.shape[0]
+    assert w_router.shape == (E, d) and w_router.dtype == x.dtype
+    dev = x.device
+    out = {"topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+           "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev)}
+    if want_logits:
+        out["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if want_probs:
+        out["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    _check(lib().moe_route(_ptr(x), _ptr(w_router), _ptr(router_bias), T, d, E, k, _dt(x),
+                           _ptr(out.get("logits")), _ptr(out.get("probs")), _ptr(out["topk_idx"]),
+                           _ptr(out["topk_w"]), _stream(stream)), "moe_route")
+    return out
+
+
+def moe_permute(topk_idx, E, stream=None):
+    """Returns (counts [E], offsets [E+1], sorted_token [T*k], inv_pos [T*k]), all int32."""
+    _dev(topk_idx)
+    assert topk_idx.dtype == torch.int32 and topk_idx.dim() == 2
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    _check(lib().moe_permute(_ptr(topk_idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(st),
+                             _ptr(inv), _stream(stream)), "moe_permute")
+    return counts, offsets, st, inv
+
+
+def _layer_shapes(x, w_gate, w_up, w_down):
+    T, d = x.shape
+    E, ffn, d2 = w_gate.shape
+    assert d2 == d and w_up.shape == (E, ffn, d) and w_down.shape == (E, d, ffn)
+    assert w_gate.dtype == w_up.dtype == w_down.dtype == x.dtype
+    return T, d, ffn, E
+
+
+def moe_expert_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, out_dtype=torch.float32, out=None,
+                   ws=None, stream=None):
+    """Expert half of the layer for a given routing; returns out [T, d]."""
+    _dev(x, topk_idx, topk_w, w_gate, w_up, w_down, out, ws)
+    T, d, ffn, E = _layer_shapes(x, w_gate, w_up, w_down)
+    k = topk_idx.shape[1]
+    assert topk_idx.dtype == torch.int32 and topk_w.dtype == torch.float32
+    assert topk_idx.shape == (T, k) and topk_w.shape == (T, k)
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=x.device)
+    if ws is None:
+        ws = workspace(T, d, ffn, E, k, x.dtype, x.device)
+    wp, wn = _ws_ptr(ws)
+    _check(lib().moe_expert_ffn(_ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(w_gate), _ptr(w_up),
+                                _ptr(w_down), T, d, ffn, E, k, _dt(x), _ptr(out), _dt(out), wp, wn,
+                                _stream(stream)), "moe_expert_ffn")
+    return out
+
+
+def moe_forward(x, w_router, w_gate, w_up, w_down, k, router_bias=None, out_dtype=torch.float32,
+                out=None, ws=None, want_logits=False, want_probs=False, want_counts=False,
+                stream=None):
+    """The whole layer. Returns out [T, d], or (out, extras) when any want_*
+    flag is set (extras: logits [T,E], probs [T,E], counts [E])."""
+    _dev(x, w_router, w_gate, w_up, w_down, router_bias, out, ws)
+    T, d, ffn, E = _layer_shapes(x, w_gate, w_up, w_down)
+    assert w_router.shape == (E, d) and w_router.dtype == x.dtype
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=dev)
+    if ws is None:
+        ws = workspace(T, d, ffn, E, k, x.dtype, dev)
+    extras = {}
+    if want_logits:
+        extras["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if want_probs:
+        extras["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if want_counts:
+        extras["counts"] = torch.empty(E, dtype=torch.int32, device=dev)
+    wp, wn = _ws_ptr(ws)
+    _check(lib().moe_forward(_ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                             _ptr(router_bias), T, d, ffn, E, k, _dt(x), _ptr(out), _dt(out),
+                             _ptr(extras.get("logits")), _ptr(extras.get("probs")),
+                             _ptr(extras.get("counts")), wp, wn, _stream(stream)), "moe_forward")
+    return (out, extras) if extras else out

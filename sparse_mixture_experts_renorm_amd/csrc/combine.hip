@@ -1,0 +1,99 @@
+// Deterministic weighted combine: out[t] = sum_{j<k} w[t,j] * y[inv_pos[t*k+j]].
+//
+// axonml-nn MoELayer::forward scatter-adds each expert's weighted output
+// into a zero buffer; the Mixtral page's _moe_forward does the same with
+// out[rows] += w * expert(x[rows]). Here each output row gathers its k
+// expert rows instead, so no two threads write one element and no float
+// atomics are needed; the k terms are added in slot order (j = 0..k-1) in
+// fp32, which fixes the rounding independently of scheduling.
+//
+// Each thread owns 8 consecutive columns of one token (16-byte loads of
+// bf16 y, 32-byte fp32 stores); a workgroup covers 2048 columns.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <typename YT>
+__device__ __forceinline__ void load8(const YT* p, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename OT>
+__device__ __forceinline__ void store8(OT* p, const float v[8]);
+
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <>
+__device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float v[8]) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
+template <typename YT, typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
+                                                      const int32_t* __restrict__ inv_pos,
+                                                      const float* __restrict__ w, int d, int k,
+                                                      OT* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (col >= d) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int p = inv_pos[static_cast<size_t>(t) * k + j];
+    if (p < 0) continue;
+    const float wj = w[static_cast<size_t>(t) * k + j];
+    float v[8];
+    load8<YT>(y + static_cast<size_t>(p) * d + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+  }
+  store8<OT>(out + static_cast<size_t>(t) * d + col, acc);
+}
+
+template <typename YT>
+void launch_typed(const void* y, const int32_t* inv_pos, const float* w, int T, int d, int k,
+                  void* out, moe_dtype out_dt, hipStream_t s) {
+  dim3 grid(T, (d + 2047) / 2048);
+  if (out_dt == MOE_F32)
+    combine_kernel<YT, float><<<grid, 256, 0, s>>>(static_cast<const YT*>(y), inv_pos, w, d, k,
+                                                   static_cast<float*>(out));
+  else
+    combine_kernel<YT, bf16_t><<<grid, 256, 0, s>>>(static_cast<const YT*>(y), inv_pos, w, d, k,
+                                                    static_cast<bf16_t*>(out));
+}
+
+}  // namespace
+
+moe_status launch_combine(const void* y, const int32_t* inv_pos, const float* topk_w, int T,
+                          int d, int k, moe_dtype y_dt, void* out, moe_dtype out_dt,
+                          hipStream_t s) {
+  if (y_dt == MOE_F32)
+    launch_typed<float>(y, inv_pos, topk_w, T, d, k, out, out_dt, s);
+  else
+    launch_typed<bf16_t>(y, inv_pos, topk_w, T, d, k, out, out_dt, s);
+  return launch_status();
+}
+
+}  // namespace moe

@@ -1,0 +1,94 @@
+// Internal helpers shared by the HIP kernels of the MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;         // CDNA wavefront width
+constexpr int kMaxExperts = 256;  // library limit on E
+constexpr int kMaxTopK = 16;      // library limit on k
+
+typedef uint16_t bf16_t;          // bfloat16 storage (bit pattern)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// SiLU(z) = z * sigmoid(z), in fp32.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Host-side launch helpers return this when a launch failed.
+inline moe_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
+}
+
+// Layout of the caller's workspace (all regions 256-byte aligned).
+struct Workspace {
+  int32_t* topk_idx;      // [T*k]
+  float* topk_w;          // [T*k]
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* sorted_token;  // [T*k]
+  int32_t* inv_pos;       // [T*k]
+  void* h;                // [T*k, ffn] in dt
+  void* y;                // [T*k, d] in dt
+  size_t bytes;
+};
+
+inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k, moe_dtype dt) {
+  const size_t tk = static_cast<size_t>(T) * k;
+  const size_t es = dt == MOE_BF16 ? 2 : 4;
+  Workspace w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) { char* r = p ? p + off : nullptr; off += align256(n); return r; };
+  w.topk_idx = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.topk_w = reinterpret_cast<float*>(take(tk * 4));
+  w.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(E) * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take(static_cast<size_t>(E + 1) * 4));
+  w.sorted_token = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.inv_pos = reinterpret_cast<int32_t*>(take(tk * 4));
+  w.h = take(tk * static_cast<size_t>(ffn) * es);
+  w.y = take(tk * static_cast<size_t>(d) * es);
+  w.bytes = off;
+  return w;
+}
+
+// ---- launchers (defined in the kernel files) ----
+moe_status launch_route(const void* x, const void* w_router, const float* bias, int T, int d,
+                        int E, int k, moe_dtype dt, float* logits, float* probs,
+                        int32_t* topk_idx, float* topk_w, hipStream_t s);
+moe_status launch_route_logits(const float* logits, int T, int E, int k, float* probs,
+                               int32_t* topk_idx, float* topk_w, hipStream_t s);
+moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
+                          hipStream_t s);
+moe_status launch_expert_gemms(const void* x, const int32_t* sorted_token, const int32_t* offsets,
+                               const void* w_gate, const void* w_up, const void* w_down, int T,
+                               int d, int ffn, int E, int k, moe_dtype dt, void* h, void* y,
+                               hipStream_t s);
+moe_status launch_combine(const void* y, const int32_t* inv_pos, const float* topk_w, int T,
+                          int d, int k, moe_dtype y_dt, void* out, moe_dtype out_dt,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,146 @@
+// C ABI of the MoE layer: argument checks, workspace carving, kernel launches.
+// Every entry point validates on the host first and enqueues nothing when an
+// argument is rejected. No entry point allocates or frees device memory.
+#include <cstdint>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+// k in 1..E follows axonml-nn MoERouter::new and KempnerForge's ModelConfig
+// MoE validation; the remaining limits are this library's.
+moe_status check_routing(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_INVALID_ARG;
+  if (E > kMaxExperts || k > kMaxTopK) return MOE_UNSUPPORTED;
+  if (static_cast<long long>(T) * k >= (1ll << 31)) return MOE_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_layer(int T, int d, int ffn, int E, int k, moe_dtype dt) {
+  if (d < 1 || ffn < 1) return MOE_INVALID_ARG;
+  moe_status st = check_routing(T, E, k);
+  if (st != MOE_OK) return st;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_UNSUPPORTED;
+  if (d % 16 != 0 || ffn % 16 != 0) return MOE_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool ok_dtype(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_INVALID_ARG: return "MOE_INVALID_ARG";
+    case MOE_UNSUPPORTED: return "MOE_UNSUPPORTED";
+    case MOE_WORKSPACE_TOO_SMALL: return "MOE_WORKSPACE_TOO_SMALL";
+    case MOE_HIP_ERROR: return "MOE_HIP_ERROR";
+  }
+  return "MOE_UNKNOWN_STATUS";
+}
+
+size_t moe_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt) {
+  if (check_layer(T, d, ffn, E, k, dt) != MOE_OK) return 0;
+  return carve_workspace(nullptr, T, d, ffn, E, k, dt).bytes;
+}
+
+moe_status moe_route_logits(const float* logits, int T, int E, int k, float* probs,
+                            int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  moe_status st = check_routing(T, E, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(topk_idx) || !ok_ptr(topk_w) || !ok_opt(probs))
+    return MOE_INVALID_ARG;
+  return launch_route_logits(logits, T, E, k, probs, topk_idx, topk_w, stream);
+}
+
+moe_status moe_route(const void* x, const void* w_router, const float* router_bias, int T, int d,
+                     int E, int k, moe_dtype dt, float* logits, float* probs, int32_t* topk_idx,
+                     float* topk_w, hipStream_t stream) {
+  if (d < 1) return MOE_INVALID_ARG;
+  moe_status st = check_routing(T, E, k);
+  if (st != MOE_OK) return st;
+  if (!ok_dtype(dt) || d % 16 != 0) return MOE_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(topk_idx) || !ok_ptr(topk_w) ||
+      !ok_opt(router_bias) || !ok_opt(logits) || !ok_opt(probs))
+    return MOE_INVALID_ARG;
+  return launch_route(x, w_router, router_bias, T, d, E, k, dt, logits, probs, topk_idx, topk_w,
+                      stream);
+}
+
+moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
+                       hipStream_t stream) {
+  moe_status st = check_routing(T, E, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(topk_idx) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(sorted_token) ||
+      !ok_ptr(inv_pos))
+    return MOE_INVALID_ARG;
+  return launch_permute(topk_idx, T, E, k, counts, offsets, sorted_token, inv_pos, stream);
+}
+
+static moe_status run_experts(const void* x, const int32_t* topk_idx, const float* topk_w,
+                              const void* w_gate, const void* w_up, const void* w_down, int T,
+                              int d, int ffn, int E, int k, moe_dtype dt, void* out,
+                              moe_dtype out_dt, const Workspace& ws, int32_t* counts_out,
+                              hipStream_t stream) {
+  moe_status st = launch_permute(topk_idx, T, E, k, counts_out ? counts_out : ws.counts,
+                                 ws.offsets, ws.sorted_token, ws.inv_pos, stream);
+  if (st != MOE_OK) return st;
+  st = launch_expert_gemms(x, ws.sorted_token, ws.offsets, w_gate, w_up, w_down, T, d, ffn, E, k,
+                           dt, ws.h, ws.y, stream);
+  if (st != MOE_OK) return st;
+  return launch_combine(ws.y, ws.inv_pos, topk_w, T, d, k, dt, out, out_dt, stream);
+}
+
+moe_status moe_expert_ffn(const void* x, const int32_t* topk_idx, const float* topk_w,
+                          const void* w_gate, const void* w_up, const void* w_down, int T, int d,
+                          int ffn, int E, int k, moe_dtype dt, void* out, moe_dtype out_dt,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_layer(T, d, ffn, E, k, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_dtype(out_dt)) return MOE_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(topk_idx) || !ok_ptr(topk_w) || !ok_ptr(w_gate) || !ok_ptr(w_up) ||
+      !ok_ptr(w_down) || !ok_ptr(out) || !ok_ptr(ws) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return MOE_INVALID_ARG;
+  const Workspace w = carve_workspace(ws, T, d, ffn, E, k, dt);
+  if (ws_bytes < w.bytes) return MOE_WORKSPACE_TOO_SMALL;
+  return run_experts(x, topk_idx, topk_w, w_gate, w_up, w_down, T, d, ffn, E, k, dt, out, out_dt,
+                     w, nullptr, stream);
+}
+
+moe_status moe_forward(const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                       const void* w_down, const float* router_bias, int T, int d, int ffn, int E,
+                       int k, moe_dtype dt, void* out, moe_dtype out_dt, float* logits_out,
+                       float* probs_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_layer(T, d, ffn, E, k, dt);
+  if (st != MOE_OK) return st;
+  if (!ok_dtype(out_dt)) return MOE_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(w_gate) || !ok_ptr(w_up) || !ok_ptr(w_down) ||
+      !ok_ptr(out) || !ok_opt(router_bias) || !ok_opt(logits_out) || !ok_opt(probs_out) ||
+      !ok_opt(counts_out) || !ok_ptr(ws) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return MOE_INVALID_ARG;
+  const Workspace w = carve_workspace(ws, T, d, ffn, E, k, dt);
+  if (ws_bytes < w.bytes) return MOE_WORKSPACE_TOO_SMALL;
+  st = launch_route(x, w_router, router_bias, T, d, E, k, dt, logits_out, probs_out, w.topk_idx,
+                    w.topk_w, stream);
+  if (st != MOE_OK) return st;
+  return run_experts(x, w.topk_idx, w.topk_w, w_gate, w_up, w_down, T, d, ffn, E, k, dt, out,
+                     out_dt, w, counts_out, stream);
+}
+
+}  // extern "C"

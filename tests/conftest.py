@@ -23,3 +23,12 @@ def golden():
         with open(os.path.join(GOLDEN, name)) as f:
             return json.load(f)
     return load
+
+
+@pytest.fixture(autouse=True)
+def _name_gpu_case(request):
+    """Write the GPU case's name (unbuffered, past pytest's capture) before it runs."""
+    if request.node.get_closest_marker("gpu"):
+        sys.__stderr__.write(f"[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments on the host before any
+device work (these calls return before touching the GPU)."""
+import ctypes
+
+import pytest
+
+import sparse_mixture_experts_renorm_amd as m
+from sparse_mixture_experts_renorm_amd import _lib
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    return m.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = m.declared_symbols()
+    assert set(names) == {"moe_status_string", "moe_workspace_size", "moe_route",
+                          "moe_route_logits", "moe_permute", "moe_expert_ffn", "moe_forward"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, s in enumerate(["MOE_OK", "MOE_INVALID_ARG", "MOE_UNSUPPORTED",
+                              "MOE_WORKSPACE_TOO_SMALL", "MOE_HIP_ERROR"]):
+        assert m.status_string(code) == s
+    assert m.status_string(99) == "MOE_UNKNOWN_STATUS"
+
+
+def test_workspace_size(L):
+    T, d, ffn, E, k = 4096, 4096, 14336, 8, 2
+    n = m.moe_workspace_size(T, d, ffn, E, k, BF16)
+    assert n >= T * k * (ffn + d) * 2 + 4 * T * k * 4
+    assert n % 256 == 0
+    assert m.moe_workspace_size(T, d, ffn, E, k, F32) > n
+    assert m.moe_workspace_size(T, d, ffn, E, 0, BF16) == 0      # k < 1
+    assert m.moe_workspace_size(T, d, ffn, E, 9, BF16) == 0      # k > E
+    assert m.moe_workspace_size(T, 4095, ffn, E, k, BF16) == 0   # d % 16
+    assert m.moe_workspace_size(T, d, ffn, 300, k, BF16) == 0    # E > 256
+    assert m.moe_workspace_size(0, d, ffn, E, k, BF16) > 0       # T = 0 is valid
+
+
+def _route_logits(L, T, E, k, ptr=16):
+    p = ctypes.c_void_p(ptr)
+    return L.moe_route_logits(p, T, E, k, None, p, p, None)
+
+
+def test_route_logits_validation(L):
+    # the page's rules: 1 <= k <= E (axonml MoERouter::new, KempnerForge ModelConfig)
+    assert _route_logits(L, 10, 8, 0) == INVALID
+    assert _route_logits(L, 10, 8, 9) == INVALID
+    assert _route_logits(L, 10, 0, 1) == INVALID
+    assert _route_logits(L, -1, 8, 2) == INVALID
+    assert _route_logits(L, 10, 300, 2) == UNSUPPORTED
+    assert _route_logits(L, 10, 32, 17) == UNSUPPORTED
+    assert _route_logits(L, 0, 8, 2, ptr=0) == OK          # T = 0: no launch
+    assert L.moe_route_logits(None, 10, 8, 2, None, None, None, None) == INVALID
+    assert _route_logits(L, 10, 8, 2, ptr=8) == INVALID    # misaligned
+
+
+def test_forward_validation(L):
+    p = ctypes.c_void_p(256)
+    base = dict(T=16, d=64, ffn=64, E=4, k=2, dt=BF16, odt=F32)
+
+    def call(ws_bytes=1 << 30, **kw):
+        a = {**base, **kw}
+        return L.moe_forward(p, p, p, p, p, None, a["T"], a["d"], a["ffn"], a["E"], a["k"],
+                             a["dt"], p, a["odt"], None, None, None, p, ws_bytes, None)
+
+    assert call(k=0) == INVALID
+    assert call(k=5) == INVALID
+    assert call(d=0) == INVALID
+    assert call(ffn=-16) == INVALID
+    assert call(d=72) == UNSUPPORTED
+    assert call(ffn=40) == UNSUPPORTED
+    assert call(dt=7) == UNSUPPORTED
+    assert call(odt=7) == UNSUPPORTED
+    assert call(ws_bytes=100) == WS_SMALL
+    assert call(T=0) == OK
+    assert L.moe_forward(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, None, F32, None, None,
+                         None, p, 1 << 30, None) == INVALID
+    # workspace must be 256-byte aligned
+    assert L.moe_forward(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, p, F32, None, None, None,
+                         ctypes.c_void_p(272), 1 << 30, None) == INVALID
+
+
+def test_expert_ffn_and_permute_validation(L):
+    p = ctypes.c_void_p(256)
+    assert L.moe_expert_ffn(p, p, p, p, p, p, 8, 64, 64, 4, 5, BF16, p, F32, p, 1 << 30, None) == INVALID
+    assert L.moe_expert_ffn(p, p, p, p, p, p, 8, 64, 64, 4, 2, BF16, p, F32, p, 10, None) == WS_SMALL
+    assert L.moe_permute(p, 8, 4, 5, p, p, p, p, None) == INVALID
+    assert L.moe_permute(p, 8, 257, 2, p, p, p, p, None) == UNSUPPORTED
+    assert L.moe_permute(None, 8, 4, 2, p, p, p, p, None) == INVALID
+    assert L.moe_route(p, p, None, 8, 40, 4, 2, BF16, None, None, p, p, None) == UNSUPPORTED
+
+
+def test_binding_requires_library(monkeypatch, tmp_path):
+    """No fallback: without the built library every binding call raises."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

@@ -1,0 +1,217 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle.
+
+Bars (written in each test): routing indices, counts, offsets and the
+permutation bit-exact when both sides get the same fp32 logits; gate weights
+and probabilities within 1e-6; layer outputs within 1e-4 x RMS (fp32
+workloads) or 2e-2 x RMS (bf16 workloads) of the fp64 oracle, max-abs over
+every compared element; bit-identical results on repeated calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as wl
+from oracle import moe_oracle as O
+from parity_util import (check_slot_order, compare_layer, dev_tensor, host, logit_tolerance,
+                         routing_alternatives, say)
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def M():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_mixture_experts_renorm_amd as m
+    m.lib()
+    return m
+
+
+# ------------------------------------------------------------ routing --
+
+ROUTE_SHAPES = [(1, 1, 1), (37, 4, 2), (300, 8, 2), (129, 13, 5), (77, 64, 8), (33, 256, 16),
+                (64, 8, 8), (1000, 2, 1)]
+
+
+@pytest.mark.parametrize("kind", wl.LOGIT_KINDS)
+@pytest.mark.parametrize("T,E,k", ROUTE_SHAPES)
+def test_route_logits_bitexact(M, kind, T, E, k):
+    say(f"moe_route_logits kind={kind} T={T} E={E} k={k}")
+    L = wl.make_logits(T, E, kind, seed=T + E)
+    idx, w, p = M.moe_route_logits(dev_tensor(L), k, probs=True)
+    torch.cuda.synchronize()
+    p_ref, idx_ref, w_ref = O.route(L, k)
+    assert np.array_equal(host(idx), idx_ref), "indices differ"
+    assert np.max(np.abs(host(w) - w_ref)) <= 1e-6
+    assert np.max(np.abs(host(p) - p_ref)) <= 1e-6
+
+
+@pytest.mark.parametrize("kind", wl.ROUTING_KINDS)
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (513, 8, 2), (2048, 8, 2), (3000, 64, 8),
+                                   (100, 256, 16), (700, 6, 3), (5000, 1, 1)])
+def test_permute_bitexact(M, kind, T, E, k):
+    if kind == "even_only" and 2 * k > E:
+        pytest.skip("needs 2k <= E")
+    if kind == "one_heavy" and E < 2 and k > 1:
+        pytest.skip("needs E >= 2")
+    say(f"moe_permute kind={kind} T={T} E={E} k={k}")
+    idx, _ = wl.make_routing(T, E, k, kind, seed=T)
+    counts, offsets, st, inv = M.moe_permute(dev_tensor(idx), E)
+    torch.cuda.synchronize()
+    c_ref, o_ref, st_ref, inv_ref = O.permute(idx, E)
+    assert np.array_equal(host(counts), c_ref)
+    assert np.array_equal(host(offsets), o_ref)
+    assert np.array_equal(host(st), st_ref)
+    assert np.array_equal(host(inv), inv_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,k,bias", [(64, 64, 4, 2, False), (300, 256, 8, 2, False),
+                                          (1000, 2048, 64, 8, True), (31, 4096, 8, 2, False),
+                                          (20, 112, 200, 16, True)])
+def test_route_fused(M, dtype, T, d, E, k, bias):
+    say(f"moe_route dtype={dtype} T={T} d={d} E={E} k={k} bias={bias}")
+    inp = wl.make_custom_inputs(T, d, 16, E, dtype, seed=3, bias=bias)
+    x, wr, b = inp["x"], inp["w_router"], inp["router_bias"]
+    r = M.moe_route(dev_tensor(x), dev_tensor(wr), k, router_bias=dev_tensor(b),
+                    want_logits=True, want_probs=True)
+    torch.cuda.synchronize()
+    L_ref = O.router_logits(x, wr, b)
+    tol = logit_tolerance(x, wr)
+    L_gpu = host(r["logits"]).astype(np.float64)
+    assert np.all(np.abs(L_gpu - L_ref) <= tol), f"max logit err {np.abs(L_gpu - L_ref).max():.3e}"
+    # routing: the oracle's own logits decide; tokens whose k-th and (k+1)-th
+    # logits are within the tolerance band may take either expert
+    alts = routing_alternatives(L_ref, k, tol)
+    gi = host(r["topk_idx"])
+    check_slot_order(gi, L_ref, tol)
+    p_ref, idx_ref, w_ref = O.route(L_ref, k)
+    for t in range(T):
+        assert tuple(sorted(gi[t].tolist())) in alts[t], (t, gi[t], alts[t])
+    # weights and probabilities: fp32 rounding plus the logit error
+    # (d p / d L is at most 1/2 per unit of logit), on unambiguous tokens
+    sure = [t for t in range(T) if len(alts[t]) == 1 and np.array_equal(gi[t], idx_ref[t])]
+    slack = 1e-6 + tol.max(axis=1)[sure, None]
+    assert np.all(np.abs(host(r["topk_w"])[sure] - w_ref[sure]) <= slack)
+    assert np.all(np.abs(host(r["probs"])[sure] - p_ref[sure]) <= slack)
+
+
+# ------------------------------------------------------- expert path --
+
+EXPERT_SHAPES = [
+    # T, d, ffn, E, k, dtype, routing kind
+    (64, 64, 128, 4, 2, "f32", "random"),
+    (300, 256, 320, 8, 2, "bf16", "random"),
+    (257, 272, 336, 8, 2, "bf16", "random"),      # ragged K and N tails
+    (200, 128, 192, 8, 3, "bf16", "all_same"),    # experts 3..7 empty
+    (333, 128, 256, 8, 2, "bf16", "even_only"),   # odd experts empty
+    (150, 192, 160, 6, 3, "bf16", "one_heavy"),   # one expert takes every token
+    (1, 64, 64, 4, 2, "bf16", "random"),
+    (40, 64, 96, 1, 1, "bf16", "random"),
+    (90, 96, 112, 5, 5, "bf16", "random"),       # k = E
+]
+
+
+@pytest.mark.parametrize("T,d,ffn,E,k,dtype,kind", EXPERT_SHAPES)
+def test_expert_ffn_parity(M, T, d, ffn, E, k, dtype, kind):
+    say(f"moe_expert_ffn T={T} d={d} ffn={ffn} E={E} k={k} {dtype} {kind}")
+    inp = wl.make_custom_inputs(T, d, ffn, E, dtype, seed=5)
+    idx, w = wl.make_routing(T, E, k, kind, seed=6)
+    args = [dev_tensor(inp[n]) for n in ("w_gate", "w_up", "w_down")]
+    out = M.moe_expert_ffn(dev_tensor(inp["x"]), dev_tensor(idx), dev_tensor(w), *args)
+    torch.cuda.synchronize()
+    ref = O.expert_ffn(inp["x"], idx, w, inp["w_gate"], inp["w_up"], inp["w_down"], E)
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(host(out).astype(np.float64) - ref).max()
+    assert err <= REL_TOL[dtype] * rms, f"max err {err / rms:.3e} x RMS"
+
+
+# -------------------------------------------------------- whole layer --
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_forward_parity_workload(M, name):
+    w = wl.WORKLOADS[name]
+    say(f"moe_forward workload={name} T={w.T} d={w.d} ffn={w.ffn} E={w.E} k={w.k}")
+    inp = wl.make_layer_inputs(w, seed=0)
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    out, ex = M.moe_forward(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k,
+                            router_bias=dv["router_bias"], want_counts=True)
+    torch.cuda.synchronize()
+    st = compare_layer(host(out), inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                       inp["w_down"], w.k, inp["router_bias"], REL_TOL[w.dtype])
+    say(f"  {name}: max err {st['max_rel_err']:.3e} x RMS, near-ties {st['near_ties']}")
+    # expert counts: exact unless a near-tie token moved between experts
+    diff = np.abs(host(ex["counts"]).astype(np.int64) - O.expert_counts(st["ref_idx"], w.E))
+    assert diff.sum() <= 2 * st["near_ties"]
+
+
+@pytest.mark.parametrize("T,d,ffn,E,k,bias", [(1, 64, 64, 4, 2, False), (129, 128, 176, 8, 2, True),
+                                              (700, 256, 512, 16, 4, True)])
+def test_forward_parity_shapes(M, T, d, ffn, E, k, bias):
+    say(f"moe_forward T={T} d={d} ffn={ffn} E={E} k={k} bias={bias}")
+    inp = wl.make_custom_inputs(T, d, ffn, E, "bf16", seed=9, bias=bias)
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    out = M.moe_forward(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], k,
+                        router_bias=dv["router_bias"])
+    torch.cuda.synchronize()
+    compare_layer(host(out), inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                  k, inp["router_bias"], REL_TOL["bf16"])
+
+
+def test_forward_zero_tokens(M):
+    say("moe_forward T=0")
+    inp = wl.make_custom_inputs(4, 64, 64, 4, "bf16")
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    x0 = dv["x"][:0]
+    out = M.moe_forward(x0, dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], 2)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_forward_deterministic_and_permutation(M):
+    """Two calls are bit-identical; permuting the tokens permutes the output
+    rows bit-exactly (tokens are independent, combine sums in slot order)."""
+    w = wl.WORKLOADS["small"]
+    say("moe_forward determinism / token permutation (small workload)")
+    inp = wl.make_layer_inputs(w, seed=1)
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    args = (dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k)
+    o1 = M.moe_forward(dv["x"], *args)
+    o2 = M.moe_forward(dv["x"], *args)
+    pi = torch.from_numpy(np.random.default_rng(0).permutation(w.T)).cuda()
+    o3 = M.moe_forward(dv["x"][pi].contiguous(), *args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(o3, o1[pi])
+
+
+def test_forward_bf16_output(M):
+    """bf16 output = the fp32 output rounded once (within 1 bf16 ulp)."""
+    w = wl.WORKLOADS["small"]
+    say("moe_forward bf16 output (small workload)")
+    inp = wl.make_layer_inputs(w, seed=2)
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    args = (dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k)
+    o32 = M.moe_forward(*args).double()
+    o16 = M.moe_forward(*args, out_dtype=torch.bfloat16).double()
+    torch.cuda.synchronize()
+    ulp = torch.abs(o32) * 2.0 ** -7 + 1e-30
+    assert torch.all(torch.abs(o16 - o32) <= ulp)
+
+
+def test_constant_input_identical_rows(M):
+    """The pages' unit-test input (every entry 0.1): every token routes the
+    same way, all k chosen experts get T rows, and all output rows match."""
+    T, d, ffn, E, k = 10, 64, 256, 4, 2
+    say("moe_forward constant 0.1 input")
+    inp = wl.make_custom_inputs(T, d, ffn, E, "bf16", seed=4)
+    x = wl.f32_to_bf16_bits(np.full((T, d), 0.1, np.float32))
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    out, ex = M.moe_forward(dev_tensor(x), dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"],
+                            k, want_counts=True)
+    torch.cuda.synchronize()
+    c = host(ex["counts"])
+    assert c.sum() == T * k and sorted(c)[-k:] == [T] * k
+    o = host(out)
+    assert np.all(o == o[0])
