@@ -1,0 +1,171 @@
+#!/usr/bin/env python3
+"""Benchmark of the top-k routed MoE layer forward on one MI355X.
+
+One step = one moe_forward call (router, softmax/top-k/renorm, permutation,
+grouped gate/up GEMM with SiLU*mul, grouped down GEMM, combine) over the
+whole batch, inputs resident in HBM. Default workload: the Mixtral-shaped
+prefill layer (T=4096, d=4096, ffn=14336, E=8, top-2, bf16 weights and
+activations, fp32 accumulation, fp32 output).
+
+Prints one JSON line: tokens/s for the layer, plus
+  roofline     -- the gate/up GEMM (the dominant kernel): its algorithmic
+                  FLOPs (4*T*k*d*ffn) per launch over its mean duration, timed
+                  with HIP events recorded between the layer's kernels on its
+                  stream, against the bf16 dense MFMA peak (prefill-like
+                  workloads) or its algorithmic bytes against HBM (decode);
+  cpu_baseline -- the CPU oracle timed on this host on a bounded token sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE layer tokens/sec + % bf16 MFMA peak (active FLOPs), d4096/ffn14336/E8/top2"
+CPU_SAMPLE = {"tiny": 64, "small": 2048, "prefill": 4096, "decode": 32, "skewed": 8192}
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["tiny", "small", "prefill", "decode", "skewed"])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (profiling runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_workloads as wl
+    import sparse_mixture_experts_renorm_amd as moe
+
+    w = wl.WORKLOADS[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    log(f"workload {w}: generating seeded inputs")
+    t0 = time.time()
+    inp = wl.make_layer_inputs(w, seed=0)
+    log(f"inputs ready in {time.time() - t0:.1f}s; copying to the GPU")
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    dv = {n: to_dev(v) for n, v in inp.items()}
+    out = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+    ws = moe.workspace(w.T, w.d, w.ffn, w.E, w.k, dv["x"].dtype, dev)
+    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
+    call = dict(router_bias=dv["router_bias"], out=out, ws=ws)
+    lay = (dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k)
+
+    log(f"warmup x{args.warmup}")
+    for _ in range(args.warmup):
+        moe.moe_forward(*lay, **call)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole-layer steps, events around the loop ----
+    log(f"timed x{args.steps}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        moe.moe_forward(*lay, **call)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-kernel times: events between the layer's kernels, same stream ----
+    log(f"per-kernel timing x{args.steps}")
+    evs = [moe.stage_events() for _ in range(args.steps)]
+    for s in range(args.steps):
+        _, ex = moe.moe_forward(*lay, **call, want_counts=True, stage_events=evs[s])
+    torch.cuda.synchronize()
+    names = ["router", "permute", "gate_up", "down", "combine"]
+    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, n in enumerate(names)}
+    cnt = ex["counts"].cpu().numpy()
+
+    # ---- roofline of the dominant kernel (gate/up GEMM) ----
+    rows = w.T * w.k
+    touched = int(np.count_nonzero(cnt))
+    gu_flops = 4.0 * rows * w.d * w.ffn
+    gu_bytes = touched * 2 * w.ffn * w.d * 2 + rows * w.d * 2 + rows * w.ffn * 2
+    gu_s = stage_ms["gate_up"] / 1e3
+    if rows >= 4 * w.E * 32:   # enough rows per expert to be MFMA-bound
+        roof = {"kernel": "expert_gemm_bf16_kernel<gate_up>", "bound": "mfma",
+                "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": "expert_gemm_bf16_kernel<gate_up>", "bound": "hbm",
+                "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["mean_ms"] = stage_ms["gate_up"]
+    roof["traffic"] = None
+
+    active = w.active_flops
+    layer_s = ms_per_step / 1e3
+    result = {
+        "metric": METRIC,
+        "value": w.T / layer_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "ffn": w.ffn, "E": w.E, "k": w.k,
+                   "out_dtype": "f32", "router_bias": w.zipf_bias},
+        "active_tflops": active / layer_s / 1e12,
+        "mfma_peak_frac": active / layer_s / 1e12 / PEAK_BF16_TFLOPS,
+        "stages_ms": stage_ms,
+        "expert_counts": cnt.tolist(),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        S = min(w.T, CPU_SAMPLE[w.name])
+        log(f"CPU oracle on the first {S} tokens")
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = len(os.sched_getaffinity(0))
+        t = time.perf_counter()
+        O.moe_forward(inp["x"][:S], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                      w.k, inp["router_bias"])
+        dt = time.perf_counter() - t
+        result["cpu_baseline"] = {
+            "value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {S} of the {w.T} tokens of the same seeded workload, fp64 numpy "
+                      f"oracle, all experts' weights widened, {dt:.1f}s"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

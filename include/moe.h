@@ -25,7 +25,9 @@
  *   - Each call checks its arguments on the host, enqueues its kernels on
  *     `stream` (NULL = the default stream) and returns without waiting.
  *     Outputs are valid once the caller has synchronised the stream.
- *   - On any error nothing is enqueued and no output is written.
+ *   - On an argument error (INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL)
+ *     nothing is enqueued and no output is written. MOE_HIP_ERROR means a
+ *     kernel launch failed; kernels enqueued before it may still run.
  *   - T = 0 is valid: the call returns MOE_OK and launches nothing.
  *   - Non-finite inputs are outside the contract (the page's sort cannot
  *     order NaN); they are not detected on the device.
@@ -60,7 +62,7 @@ const char* moe_status_string(moe_status s);
 
 /* Bytes of device workspace that moe_forward and moe_expert_ffn need for this
  * shape: routing results, per-expert offsets, the permutation, the hidden
- * activations h [T*k, ffn] and expert outputs y [T*k, d] (in dt). Returns 0
+ * activations h [T*k, ffn] (in dt) and expert outputs y [T*k, d] (fp32). Returns 0
  * for invalid or unsupported shapes. Host-only; no device access. */
 size_t moe_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt);
 
@@ -128,6 +130,19 @@ moe_status moe_forward(const void* x, const void* w_router, const void* w_gate,
                        void* out, moe_dtype out_dt,
                        float* logits_out, float* probs_out, int32_t* counts_out,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward that also records caller-created events on `stream` between
+ * its stages, for per-kernel timing: stage_events[0] before the router,
+ * [1] after the router, [2] after the permutation, [3] after the gate/up
+ * GEMM, [4] after the down GEMM, [5] after the combine (6 events, none NULL).
+ * Results are identical to moe_forward's. */
+moe_status moe_forward_profiled(const void* x, const void* w_router, const void* w_gate,
+                                const void* w_up, const void* w_down, const float* router_bias,
+                                int T, int d, int ffn, int E, int k, moe_dtype dt,
+                                void* out, moe_dtype out_dt,
+                                float* logits_out, float* probs_out, int32_t* counts_out,
+                                void* ws, size_t ws_bytes, hipStream_t stream,
+                                hipEvent_t* stage_events);
 
 #ifdef __cplusplus
 }

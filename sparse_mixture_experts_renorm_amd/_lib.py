@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         _p("moe_permute", i, vp, i, i, i, vp, vp, vp, vp, vp)
         _p("moe_expert_ffn", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, sz, vp)
         _p("moe_forward", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp, vp, sz, vp)
+        _p("moe_forward_profiled", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp,
+           vp, sz, vp, vp)
     return _lib
 
 
@@ -192,11 +194,24 @@ def moe_expert_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, out_dtype=torch.fl
     return out
 
 
+def stage_events():
+    """Six timing events for moe_forward(stage_events=...): before the router,
+    after it, after the permutation, the gate/up GEMM, the down GEMM and the
+    combine. Each is recorded once here so its HIP event exists."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    return evs
+
+
 def moe_forward(x, w_router, w_gate, w_up, w_down, k, router_bias=None, out_dtype=torch.float32,
                 out=None, ws=None, want_logits=False, want_probs=False, want_counts=False,
-                stream=None):
+                stream=None, stage_events=None):
     """The whole layer. Returns out [T, d], or (out, extras) when any want_*
-    flag is set (extras: logits [T,E], probs [T,E], counts [E])."""
+    flag is set (extras: logits [T,E], probs [T,E], counts [E]). With
+    stage_events (from stage_events()) it calls moe_forward_profiled, which
+    records them between the layer's kernels."""
     _dev(x, w_router, w_gate, w_up, w_down, router_bias, out, ws)
     T, d, ffn, E = _layer_shapes(x, w_gate, w_up, w_down)
     assert w_router.shape == (E, d) and w_router.dtype == x.dtype
@@ -213,8 +228,13 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, k, router_bias=None, out_dtyp
     if want_counts:
         extras["counts"] = torch.empty(E, dtype=torch.int32, device=dev)
     wp, wn = _ws_ptr(ws)
-    _check(lib().moe_forward(_ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-                             _ptr(router_bias), T, d, ffn, E, k, _dt(x), _ptr(out), _dt(out),
-                             _ptr(extras.get("logits")), _ptr(extras.get("probs")),
-                             _ptr(extras.get("counts")), wp, wn, _stream(stream)), "moe_forward")
+    args = [_ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(router_bias), T,
+            d, ffn, E, k, _dt(x), _ptr(out), _dt(out), _ptr(extras.get("logits")),
+            _ptr(extras.get("probs")), _ptr(extras.get("counts")), wp, wn, _stream(stream)]
+    if stage_events is None:
+        _check(lib().moe_forward(*args), "moe_forward")
+    else:
+        assert len(stage_events) == 6
+        arr = (ctypes.c_void_p * 6)(*[e.cuda_event for e in stage_events])
+        _check(lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
     return (out, extras) if extras else out

@@ -7,8 +7,8 @@
 // atomics are needed; the k terms are added in slot order (j = 0..k-1) in
 // fp32, which fixes the rounding independently of scheduling.
 //
-// Each thread owns 8 consecutive columns of one token (16-byte loads of
-// bf16 y, 32-byte fp32 stores); a workgroup covers 2048 columns.
+// y is fp32. Each thread owns 8 consecutive columns of one token (two
+// 16-byte loads per term); a workgroup covers 2048 columns.
 #include "common.h"
 
 namespace moe {
@@ -16,17 +16,6 @@ namespace {
 
 template <typename YT>
 __device__ __forceinline__ void load8(const YT* p, float v[8]);
-
-template <>
-__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
 
 template <>
 __device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
@@ -72,27 +61,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   store8<OT>(out + static_cast<size_t>(t) * d + col, acc);
 }
 
-template <typename YT>
-void launch_typed(const void* y, const int32_t* inv_pos, const float* w, int T, int d, int k,
-                  void* out, moe_dtype out_dt, hipStream_t s) {
-  dim3 grid(T, (d + 2047) / 2048);
-  if (out_dt == MOE_F32)
-    combine_kernel<YT, float><<<grid, 256, 0, s>>>(static_cast<const YT*>(y), inv_pos, w, d, k,
-                                                   static_cast<float*>(out));
-  else
-    combine_kernel<YT, bf16_t><<<grid, 256, 0, s>>>(static_cast<const YT*>(y), inv_pos, w, d, k,
-                                                    static_cast<bf16_t*>(out));
-}
-
 }  // namespace
 
-moe_status launch_combine(const void* y, const int32_t* inv_pos, const float* topk_w, int T,
-                          int d, int k, moe_dtype y_dt, void* out, moe_dtype out_dt,
-                          hipStream_t s) {
-  if (y_dt == MOE_F32)
-    launch_typed<float>(y, inv_pos, topk_w, T, d, k, out, out_dt, s);
+moe_status launch_combine(const float* y, const int32_t* inv_pos, const float* topk_w, int T,
+                          int d, int k, void* out, moe_dtype out_dt, hipStream_t s) {
+  dim3 grid(T, (d + 2047) / 2048);
+  if (out_dt == MOE_F32)
+    combine_kernel<float, float><<<grid, 256, 0, s>>>(y, inv_pos, topk_w, d, k,
+                                                      static_cast<float*>(out));
   else
-    launch_typed<bf16_t>(y, inv_pos, topk_w, T, d, k, out, out_dt, s);
+    combine_kernel<float, bf16_t><<<grid, 256, 0, s>>>(y, inv_pos, topk_w, d, k,
+                                                       static_cast<bf16_t*>(out));
   return launch_status();
 }
 

@@ -49,7 +49,7 @@ struct Workspace {
   int32_t* sorted_token;  // [T*k]
   int32_t* inv_pos;       // [T*k]
   void* h;                // [T*k, ffn] in dt
-  void* y;                // [T*k, d] in dt
+  float* y;               // [T*k, d] fp32
   size_t bytes;
 };
 
@@ -69,7 +69,7 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   w.sorted_token = reinterpret_cast<int32_t*>(take(tk * 4));
   w.inv_pos = reinterpret_cast<int32_t*>(take(tk * 4));
   w.h = take(tk * static_cast<size_t>(ffn) * es);
-  w.y = take(tk * static_cast<size_t>(d) * es);
+  w.y = reinterpret_cast<float*>(take(tk * static_cast<size_t>(d) * 4));
   w.bytes = off;
   return w;
 }
@@ -83,12 +83,12 @@ moe_status launch_route_logits(const float* logits, int T, int E, int k, float* 
 moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
                           hipStream_t s);
-moe_status launch_expert_gemms(const void* x, const int32_t* sorted_token, const int32_t* offsets,
-                               const void* w_gate, const void* w_up, const void* w_down, int T,
-                               int d, int ffn, int E, int k, moe_dtype dt, void* h, void* y,
-                               hipStream_t s);
-moe_status launch_combine(const void* y, const int32_t* inv_pos, const float* topk_w, int T,
-                          int d, int k, moe_dtype y_dt, void* out, moe_dtype out_dt,
-                          hipStream_t s);
+moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
+                          const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
+                          int k, moe_dtype dt, void* h, hipStream_t s);
+moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down, int T, int d,
+                       int ffn, int E, int k, moe_dtype dt, float* y, hipStream_t s);
+moe_status launch_combine(const float* y, const int32_t* inv_pos, const float* topk_w, int T,
+                          int d, int k, void* out, moe_dtype out_dt, hipStream_t s);
 
 }  // namespace moe

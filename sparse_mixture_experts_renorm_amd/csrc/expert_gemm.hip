@@ -6,6 +6,9 @@
 // X_e are the rows sorted_token[offsets[e] .. offsets[e+1]) of x: the gather
 // is done by the tile loads, so X_e is never written out. h and y are stored
 // in permuted-row order, row offsets[e] + r for the r-th token of expert e.
+// h is bf16 (the down pass multiplies it on the bf16 MFMA); y stays fp32,
+// because rounding y to bf16 as well would spend about half of the 2e-2 x RMS
+// error budget of bf16 workloads on top of h's rounding.
 //
 // bf16 path (gfx950 MFMA). A workgroup of 4 waves computes one output tile
 // of 128 permuted rows; the gate/up pass produces 64 columns of h from a
@@ -99,7 +102,7 @@ template <bool GATE_UP>
 __global__ __launch_bounds__(NT, 1) void expert_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
-    const bf16_t* __restrict__ B1, int N, int K, bf16_t* __restrict__ C) {
+    const bf16_t* __restrict__ B1, int N, int K, void* __restrict__ Cv) {
   __shared__ __attribute__((aligned(16))) char lds[2][2][BM * 128];  // [buf][A|B]
   const int nN = GATE_UP ? (N + 63) / 64 : (N + BNW - 1) / BNW;
   Tile tile;
@@ -211,17 +214,16 @@ __global__ __launch_bounds__(NT, 1) void expert_gemm_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) hv[i] = silu(acc[0][mb][4 * g + i]) * acc[1][mb][4 * g + i];
           uint2 pk = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-          *reinterpret_cast<uint2*>(C + crow + n) = pk;
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) = pk;
         }
       } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const int n = tile.nt * BNW + brow[nb] + nloc;
-          if (n < N) {
-            uint2 pk = make_uint2(pack_bf16x2(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1]),
-                                  pack_bf16x2(acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]));
-            *reinterpret_cast<uint2*>(C + crow + n) = pk;
-          }
+          if (n < N)
+            *reinterpret_cast<float4*>(static_cast<float*>(Cv) + crow + n) =
+                make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                            acc[nb][mb][4 * g + 3]);
         }
       }
     }
@@ -268,35 +270,41 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(
 
 }  // namespace
 
-moe_status launch_expert_gemms(const void* x, const int32_t* sorted_token, const int32_t* offsets,
-                               const void* w_gate, const void* w_up, const void* w_down, int T,
-                               int d, int ffn, int E, int k, moe_dtype dt, void* h, void* y,
-                               hipStream_t s) {
+// upper bound on sum_e ceil(M_e / BM) over the experts' row counts M_e
+static unsigned tile_grid(int rows, int E, int nN) {
+  const long long max_mt = rows / BM + (rows < E ? rows : E);
+  const long long g = max_mt * nN;
+  return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds);
+}
+
+moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
+                          const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
+                          int k, moe_dtype dt, void* h, hipStream_t s) {
   const int rows = T * k;
   if (dt == MOE_F32) {
-    dim3 g1(rows, (ffn + 255) / 256), g2(rows, (d + 255) / 256);
-    expert_gemm_f32_kernel<true><<<g1, 256, 0, s>>>(static_cast<const float*>(x), sorted_token,
-                                                    offsets, E, static_cast<const float*>(w_gate),
-                                                    static_cast<const float*>(w_up), ffn, d,
-                                                    static_cast<float*>(h));
-    expert_gemm_f32_kernel<false><<<g2, 256, 0, s>>>(static_cast<const float*>(h), nullptr, offsets,
-                                                     E, static_cast<const float*>(w_down), nullptr,
-                                                     d, ffn, static_cast<float*>(y));
+    expert_gemm_f32_kernel<true><<<dim3(rows, (ffn + 255) / 256), 256, 0, s>>>(
+        static_cast<const float*>(x), sorted_token, offsets, E, static_cast<const float*>(w_gate),
+        static_cast<const float*>(w_up), ffn, d, static_cast<float*>(h));
     return launch_status();
   }
-  // upper bound on sum_e ceil(M_e / BM)
-  const int max_mt = rows / BM + (rows < E ? rows : E);
-  auto grid_for = [&](int nN) {
-    long long g = static_cast<long long>(max_mt) * nN;
-    g = (g + kXcds - 1) / kXcds * kXcds;
-    return static_cast<unsigned>(g);
-  };
-  expert_gemm_bf16_kernel<true><<<grid_for((ffn + 63) / 64), NT, 0, s>>>(
+  expert_gemm_bf16_kernel<true><<<tile_grid(rows, E, (ffn + 63) / 64), NT, 0, s>>>(
       static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
-      static_cast<const bf16_t*>(w_up), ffn, d, static_cast<bf16_t*>(h));
-  expert_gemm_bf16_kernel<false><<<grid_for((d + BNW - 1) / BNW), NT, 0, s>>>(
+      static_cast<const bf16_t*>(w_up), ffn, d, h);
+  return launch_status();
+}
+
+moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down, int T, int d,
+                       int ffn, int E, int k, moe_dtype dt, float* y, hipStream_t s) {
+  const int rows = T * k;
+  if (dt == MOE_F32) {
+    expert_gemm_f32_kernel<false><<<dim3(rows, (d + 255) / 256), 256, 0, s>>>(
+        static_cast<const float*>(h), nullptr, offsets, E, static_cast<const float*>(w_down),
+        nullptr, d, ffn, y);
+    return launch_status();
+  }
+  expert_gemm_bf16_kernel<false><<<tile_grid(rows, E, (d + BNW - 1) / BNW), NT, 0, s>>>(
       static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
-      nullptr, d, ffn, static_cast<bf16_t*>(y));
+      nullptr, d, ffn, y);
   return launch_status();
 }
 

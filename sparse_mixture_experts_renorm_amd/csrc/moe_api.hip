@@ -90,18 +90,27 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* co
   return launch_permute(topk_idx, T, E, k, counts, offsets, sorted_token, inv_pos, stream);
 }
 
+// ev: NULL, or events [2..5] are recorded after the permutation, the gate/up
+// GEMM, the down GEMM and the combine.
 static moe_status run_experts(const void* x, const int32_t* topk_idx, const float* topk_w,
                               const void* w_gate, const void* w_up, const void* w_down, int T,
                               int d, int ffn, int E, int k, moe_dtype dt, void* out,
                               moe_dtype out_dt, const Workspace& ws, int32_t* counts_out,
-                              hipStream_t stream) {
+                              hipStream_t stream, hipEvent_t* ev) {
   moe_status st = launch_permute(topk_idx, T, E, k, counts_out ? counts_out : ws.counts,
                                  ws.offsets, ws.sorted_token, ws.inv_pos, stream);
   if (st != MOE_OK) return st;
-  st = launch_expert_gemms(x, ws.sorted_token, ws.offsets, w_gate, w_up, w_down, T, d, ffn, E, k,
-                           dt, ws.h, ws.y, stream);
+  if (ev) hipEventRecord(ev[2], stream);
+  st = launch_gate_up(x, ws.sorted_token, ws.offsets, w_gate, w_up, T, d, ffn, E, k, dt, ws.h,
+                      stream);
   if (st != MOE_OK) return st;
-  return launch_combine(ws.y, ws.inv_pos, topk_w, T, d, k, dt, out, out_dt, stream);
+  if (ev) hipEventRecord(ev[3], stream);
+  st = launch_down(ws.h, ws.offsets, w_down, T, d, ffn, E, k, dt, ws.y, stream);
+  if (st != MOE_OK) return st;
+  if (ev) hipEventRecord(ev[4], stream);
+  st = launch_combine(ws.y, ws.inv_pos, topk_w, T, d, k, out, out_dt, stream);
+  if (ev) hipEventRecord(ev[5], stream);
+  return st;
 }
 
 moe_status moe_expert_ffn(const void* x, const int32_t* topk_idx, const float* topk_w,
@@ -118,14 +127,15 @@ moe_status moe_expert_ffn(const void* x, const int32_t* topk_idx, const float* t
   const Workspace w = carve_workspace(ws, T, d, ffn, E, k, dt);
   if (ws_bytes < w.bytes) return MOE_WORKSPACE_TOO_SMALL;
   return run_experts(x, topk_idx, topk_w, w_gate, w_up, w_down, T, d, ffn, E, k, dt, out, out_dt,
-                     w, nullptr, stream);
+                     w, nullptr, stream, nullptr);
 }
 
-moe_status moe_forward(const void* x, const void* w_router, const void* w_gate, const void* w_up,
-                       const void* w_down, const float* router_bias, int T, int d, int ffn, int E,
-                       int k, moe_dtype dt, void* out, moe_dtype out_dt, float* logits_out,
-                       float* probs_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+static moe_status forward_impl(const void* x, const void* w_router, const void* w_gate,
+                               const void* w_up, const void* w_down, const float* router_bias,
+                               int T, int d, int ffn, int E, int k, moe_dtype dt, void* out,
+                               moe_dtype out_dt, float* logits_out, float* probs_out,
+                               int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                               hipEvent_t* ev) {
   moe_status st = check_layer(T, d, ffn, E, k, dt);
   if (st != MOE_OK) return st;
   if (!ok_dtype(out_dt)) return MOE_UNSUPPORTED;
@@ -136,11 +146,36 @@ moe_status moe_forward(const void* x, const void* w_router, const void* w_gate, 
     return MOE_INVALID_ARG;
   const Workspace w = carve_workspace(ws, T, d, ffn, E, k, dt);
   if (ws_bytes < w.bytes) return MOE_WORKSPACE_TOO_SMALL;
+  if (ev) hipEventRecord(ev[0], stream);
   st = launch_route(x, w_router, router_bias, T, d, E, k, dt, logits_out, probs_out, w.topk_idx,
                     w.topk_w, stream);
   if (st != MOE_OK) return st;
+  if (ev) hipEventRecord(ev[1], stream);
   return run_experts(x, w.topk_idx, w.topk_w, w_gate, w_up, w_down, T, d, ffn, E, k, dt, out,
-                     out_dt, w, counts_out, stream);
+                     out_dt, w, counts_out, stream, ev);
+}
+
+moe_status moe_forward(const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                       const void* w_down, const float* router_bias, int T, int d, int ffn, int E,
+                       int k, moe_dtype dt, void* out, moe_dtype out_dt, float* logits_out,
+                       float* probs_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  return forward_impl(x, w_router, w_gate, w_up, w_down, router_bias, T, d, ffn, E, k, dt, out,
+                      out_dt, logits_out, probs_out, counts_out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_profiled(const void* x, const void* w_router, const void* w_gate,
+                                const void* w_up, const void* w_down, const float* router_bias,
+                                int T, int d, int ffn, int E, int k, moe_dtype dt, void* out,
+                                moe_dtype out_dt, float* logits_out, float* probs_out,
+                                int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                                hipEvent_t* stage_events) {
+  if (!stage_events) return MOE_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
+    if (!stage_events[i]) return MOE_INVALID_ARG;
+  return forward_impl(x, w_router, w_gate, w_up, w_down, router_bias, T, d, ffn, E, k, dt, out,
+                      out_dt, logits_out, probs_out, counts_out, ws, ws_bytes, stream,
+                      stage_events);
 }
 
 }  // extern "C"

@@ -20,7 +20,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = m.declared_symbols()
     assert set(names) == {"moe_status_string", "moe_workspace_size", "moe_route",
-                          "moe_route_logits", "moe_permute", "moe_expert_ffn", "moe_forward"}
+                          "moe_route_logits", "moe_permute", "moe_expert_ffn", "moe_forward",
+                          "moe_forward_profiled"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -97,6 +98,11 @@ def test_expert_ffn_and_permute_validation(L):
     assert L.moe_permute(p, 8, 257, 2, p, p, p, p, None) == UNSUPPORTED
     assert L.moe_permute(None, 8, 4, 2, p, p, p, p, None) == INVALID
     assert L.moe_route(p, p, None, 8, 40, 4, 2, BF16, None, None, p, p, None) == UNSUPPORTED
+    ev = (ctypes.c_void_p * 6)(*([16] * 5 + [0]))
+    assert L.moe_forward_profiled(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, p, F32, None, None,
+                                  None, p, 1 << 30, None, ev) == INVALID
+    assert L.moe_forward_profiled(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, p, F32, None, None,
+                                  None, p, 1 << 30, None, None) == INVALID
 
 
 def test_binding_requires_library(monkeypatch, tmp_path):
