@@ -10,17 +10,24 @@
 // because rounding y to bf16 as well would spend about half of the 2e-2 x RMS
 // error budget of bf16 workloads on top of h's rounding.
 //
-// bf16 path (gfx950 MFMA). A workgroup of 4 waves computes one output tile
-// of 128 permuted rows; the gate/up pass produces 64 columns of h from a
-// 128-row weight tile (64 gate rows + the same 64 up rows), the down pass
-// 128 columns of y. The reduction dimension moves through LDS in steps of
-// 64 (128 bytes per row), double-buffered: the next step's global loads are
-// in flight while the current one runs on v_mfma_f32_32x32x16_bf16.
-// LDS rows are XOR-swizzled in 16-byte chunks (chunk c of row r is stored at
-// c ^ (r & 7)) so the MFMA operand reads of 32 different rows spread over
-// all banks. The MFMA takes the weight tile as its first operand, so each
-// lane's accumulators hold 4 consecutive output columns of one row, which
-// the epilogue writes as one 8-byte store.
+// bf16 path (gfx950). One workgroup of 4 waves per CU computes a 256 x 256
+// tile: 256 permuted rows against 256 weight rows (gate/up: 128 gate rows and
+// the same 128 up rows, giving 128 columns of h; down: 256 columns of y).
+// Each wave owns a 128 x 128 quarter: 16 accumulators of
+// v_mfma_f32_32x32x16_bf16 (256 fp32 per lane, held in AGPRs), so every
+// 16-byte fragment read from LDS feeds 4 MFMAs. The reduction dimension moves
+// in steps of 64 through two LDS stages (64 KB each): the loads of step s+1
+// are issued with global_load_lds_dwordx4 (memory to LDS without VGPRs) just
+// before the MFMAs of step s. Each lane supplies its own address, which is how the token gather
+// of the gate/up pass is done; lanes past K read a 16-byte zero page.
+// LDS rows are 128 bytes (64 bf16); chunk c (16 bytes) of row r is stored at
+// slot c ^ ((r >> 1) & 7). gfx950 serves a 16-byte-per-lane LDS read 16 lanes
+// at a time over 64 four-byte banks; a fragment read sends 16 consecutive
+// rows to those lanes, and the row's half of the 256-byte bank line (r & 1)
+// together with its slot gives 16 distinct bank groups.
+// The MFMA takes the weight fragment as its first operand, so each lane's
+// accumulators hold 4 consecutive output columns of one row, which the
+// epilogue writes as one 8-byte (h) or 16-byte (y) store.
 //
 // Tile schedule: the host sizes the grid from an upper bound on the tile
 // count; each workgroup reads the per-expert offsets, counts the real tiles
@@ -36,18 +43,15 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;   // permuted rows per tile
-constexpr int BNW = 128;  // weight rows per tile
-constexpr int BK = 64;    // reduction step (elements)
-constexpr int NT = 256;   // threads per workgroup
-constexpr int GN = 8;     // column tiles per schedule group
 constexpr int kXcds = 8;
+constexpr int GN = 8;     // column tiles per schedule group
 
 struct Tile {
   int e, row0, rows, nt;
 };
 
-// Map this workgroup to a tile; returns false if it has none.
+// Map this workgroup to a tile of BM rows; returns false if it has none.
+template <int BM>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, Tile* out) {
   __shared__ int s_tile[4];
   if (threadIdx.x == 0) {
@@ -94,132 +98,203 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, Til
   return true;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// 16 bytes of zeros: the source of every masked lane of a direct LDS load.
+__device__ __attribute__((aligned(64))) uint32_t g_zero_page[16];
 
-// GATE_UP: A = x gathered by sorted_token, B = [w_gate; w_up], C = h.
-// !GATE_UP: A = h (rows in order), B = w_down, C = y.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void load_lds16(const void* g, char* lds_chunk_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(lds_chunk_base), 16, 0, 0);
+}
+
+constexpr int TM = 256;        // permuted rows per tile
+constexpr int TW = 256;        // weight rows per tile
+constexpr int TK = 64;         // reduction step (elements); one LDS row = 128 bytes
+constexpr int TNT = 256;       // threads per workgroup
+constexpr int STAGE = TM * TK * 2;  // bytes per operand and stage (32 KB)
+constexpr int IPW = 8;         // 1 KB load instructions per wave, per operand and stage
+
+// GATE_UP: A = x gathered by sorted_token, weights = [w_gate; w_up], C = h (bf16).
+// !GATE_UP: A = h (rows in order), weights = w_down, C = y (fp32).
 template <bool GATE_UP>
-__global__ __launch_bounds__(NT, 1) void expert_gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
-    const int32_t* __restrict__ offsets, int E, const bf16_t* __restrict__ B0,
-    const bf16_t* __restrict__ B1, int N, int K, void* __restrict__ Cv) {
-  __shared__ __attribute__((aligned(16))) char lds[2][2][BM * 128];  // [buf][A|B]
-  const int nN = GATE_UP ? (N + 63) / 64 : (N + BNW - 1) / BNW;
+__global__ __launch_bounds__(TNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
+                             const int32_t* __restrict__ offsets, int E,
+                             const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
+                             int K, void* __restrict__ Cv) {
+  // One LDS object per stage and operand. They must be distinct objects: the
+  // compiler then sees that the memory-to-LDS loads of the next stage cannot
+  // alias the fragment reads of the current one, and does not make those
+  // reads wait for the loads.
+  __shared__ __attribute__((aligned(1024))) char lds0a[STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds0b[STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1a[STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1b[STAGE];
+  // st and op are compile-time constants at every use, so this folds away
+  auto buf = [&](int st, int op) -> char* {
+    return st == 0 ? (op ? lds0b : lds0a) : (op ? lds1b : lds1a);
+  };
+  const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
-  if (!map_tile(offsets, E, nN, &tile)) return;
+  if (!map_tile<TM>(offsets, E, nN, &tile)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Global source of the 4 A chunks and 4 B chunks this thread stages.
-  const bf16_t* a_src[4];
-  const bf16_t* b_src[4];
-  int lds_off[4];
+  // ---- direct-load sources. Per stage each operand is 256 rows x 128 bytes,
+  // loaded by 1 KB instructions of 8 rows; wave w issues instructions
+  // 8w .. 8w+7. In instruction q lane l writes row r = q*8 + l/8, slot l%8,
+  // which holds chunk (l%8) ^ ((r >> 1) & 7).
+  // Sources are 32-bit byte offsets from one base per operand. Rows past the
+  // tile's valid rows (or past N) repeat a valid row: their products are
+  // computed but never stored. Chunks past K read the zero page.
+  // Tile row r of the weight operand: gate/up rows 0-127 are gate rows
+  // n0 .. n0+127, rows 128-255 the same rows of up; down rows are n0 + r.
+  const int n0 = GATE_UP ? tile.nt * 128 : tile.nt * TW;
+  const char* a_base = reinterpret_cast<const char*>(A);
+  const size_t wexp = static_cast<size_t>(tile.e) * N * K * 2;
+  auto a_row_off = [&](int r) -> uint32_t {
+    const int rr = r < tile.rows ? r : 0;
+    const uint32_t arow = GATE_UP ? static_cast<uint32_t>(sorted_token[tile.row0 + rr])
+                                  : static_cast<uint32_t>(tile.row0 + rr);
+    return arow * static_cast<uint32_t>(K) * 2u;
+  };
+  auto b_row_off = [&](int r) -> uint32_t {
+    const int n = min(n0 + (GATE_UP ? (r & 127) : r), N - 1);
+    return static_cast<uint32_t>(n) * static_cast<uint32_t>(K) * 2u;
+  };
+  uint32_t a_off[IPW], b_off[IPW];
+  int kchunk[IPW];
+  const char* b_base[IPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = tid + NT * j;
-    const int row = q >> 3, c = q & 7;
-    lds_off[j] = swz(row, c);
-    a_src[j] = nullptr;
-    if (row < tile.rows) {
-      const size_t arow = GATE_UP ? static_cast<size_t>(sorted_token[tile.row0 + row])
-                                  : static_cast<size_t>(tile.row0 + row);
-      a_src[j] = A + arow * K + c * 8;
-    }
-    b_src[j] = nullptr;
-    if (GATE_UP) {
-      const int n = tile.nt * 64 + (row & 63);
-      if (n < N) b_src[j] = (row < 64 ? B0 : B1) + (static_cast<size_t>(tile.e) * N + n) * K + c * 8;
-    } else {
-      const int n = tile.nt * BNW + row;
-      if (n < N) b_src[j] = B0 + (static_cast<size_t>(tile.e) * N + n) * K + c * 8;
-    }
+  for (int j = 0; j < IPW; ++j) {
+    const int r = (wave * IPW + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    kchunk[j] = c;
+    a_off[j] = a_row_off(r) + c * 16u;
+    b_off[j] = b_row_off(r) + c * 16u;
+    b_base[j] = reinterpret_cast<const char*>((GATE_UP && r >= 128) ? B1 : B0) + wexp;
   }
-  const int kc_lane = (lane >> 5);  // which 8-element half of a 16-wide k step
-
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = k0 + ((tid + NT * j) & 7) * 8;
-      ra[j] = (a_src[j] && kk < K) ? *reinterpret_cast<const uint4*>(a_src[j] + k0) : make_uint4(0, 0, 0, 0);
-      rb[j] = (b_src[j] && kk < K) ? *reinterpret_cast<const uint4*>(b_src[j] + k0) : make_uint4(0, 0, 0, 0);
-    }
+  const char* zero = reinterpret_cast<const char*>(g_zero_page);
+  // load instruction j (0 .. 2*IPW-1: A then B) of step kt into stage st
+  auto issue_one = [&](int kt, int st, int j) {
+    const int k0 = kt * TK;
+    const int jj = j % IPW;
+    const bool kin = k0 + kchunk[jj] * 8 < K;
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+    if (j < IPW)
+      load_lds16(kin ? a_base + (a_off[jj] + kb) : zero, buf(st, 0) + (wave * IPW + jj) * 1024);
+    else
+      load_lds16(kin ? b_base[jj] + (b_off[jj] + kb) : zero, buf(st, 1) + (wave * IPW + jj) * 1024);
   };
-  auto sstore = [&](int buf) {
+  // ---- fragment reads: row R's chunk c is at R*128 + ((c ^ ((R >> 1) & 7)) << 4);
+  // every row this lane reads has R % 32 == lane % 32.
+  const int xr = ((lane & 31) >> 1) & 7, half = lane >> 5;
+  int fa_off[4], fb_off[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<uint4*>(&lds[buf][0][lds_off[j]]) = ra[j];
-      *reinterpret_cast<uint4*>(&lds[buf][1][lds_off[j]]) = rb[j];
-    }
-  };
+  for (int i = 0; i < 4; ++i) {
+    fa_off[i] = (wm * 128 + i * 32 + (lane & 31)) * 128;
+    const int brow = GATE_UP ? (i >> 1) * 128 + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+    fb_off[i] = (brow + (lane & 31)) * 128;
+  }
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  // weight-tile row base of the wave's two 32-row blocks
-  int brow[2];
-  brow[0] = GATE_UP ? wn * 32 : wn * 64;
-  brow[1] = GATE_UP ? 64 + wn * 32 : wn * 64 + 32;
-  const int arow0 = wm * 64 + (lane & 31);
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const char* la = lds[buf][0];
-    const char* lb = lds[buf][1];
+  auto read_frags = [&](int st, int s, bf16x8* fa, bf16x8* fb) {
+    const int slot = ((2 * s + half) ^ xr) << 4;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int c = 2 * s + kc_lane;
-      bf16x8 fa[2], fb[2];
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(buf(st, 0) + fa_off[i] + slot);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        fa[mb] = *reinterpret_cast<const bf16x8*>(la + swz(arow0 + mb * 32, c));
+    for (int i = 0; i < 4; ++i) fb[i] = *reinterpret_cast<const bf16x8*>(buf(st, 1) + fb_off[i] + slot);
+  };
+  auto mma16 = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        fb[nb] = *reinterpret_cast<const bf16x8*>(lb + swz(brow[nb] + (lane & 31), c));
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int mb = 0; mb < 4; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+  };
+  // One step on stage st: the next step's loads go out first, as one burst
+  // (a load that waits for a free slot in the memory pipeline then delays
+  // the MFMAs once per step, not between every few MFMAs); then, while the
+  // 16 MFMAs of substep s run, the fragment reads of substep s+1 are issued.
+  auto step = [&](int kt, int st, bool next) {
+    if (next) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+      for (int j = 0; j < 2 * IPW; ++j) issue_one(kt + 1, st ^ 1, j);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue. acc[nb][mb] element i: token row wm*64 + mb*32 + lane%32,
-  // weight-tile row brow[nb] + 8*(i/4) + 4*(lane/32) + i%4.
+    bf16x8 fa[2][4], fb[2][4];
+    read_frags(st, 0, fa[0], fb[0]);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = wm * 64 + mb * 32 + (lane & 31);
+    for (int s = 0; s < TK / 16; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < TK / 16) read_frags(st, s + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      mma16(fa[cur], fb[cur]);
+      if (s + 1 < TK / 16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 fragment read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+    }
+  };
+
+  // Before step kt is computed its loads must have landed in LDS (each wave
+  // waits for its own); the barrier then makes every wave's loads visible
+  // and guarantees that the other stage, overwritten during step kt, is no
+  // longer read. The step count is rounded up to even; a step past K loads
+  // zeros.
+  const int nk = (K + TK - 1) / TK;
+  const int nk2 = (nk + 1) & ~1;
+#pragma unroll
+  for (int j = 0; j < 2 * IPW; ++j) issue_one(0, 0, j);
+  for (int kt0 = 0; kt0 < nk2; kt0 += 2) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int kt = kt0 + r;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      step(kt, r, kt + 1 < nk2);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue. acc[nb][mb] element i: token row wm*128 + mb*32 + lane%32,
+  // weight-tile row (block nb) + 8*(i/4) + 4*(lane/32) + i%4.
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = wm * 128 + mb * 32 + (lane & 31);
     if (m >= tile.rows) continue;
     const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int nloc = 8 * g + 4 * (lane >> 5);
+      const int nloc = 8 * g + 4 * half;
       if (GATE_UP) {
-        const int n = tile.nt * 64 + wn * 32 + nloc;
-        if (n < N) {
-          float hv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) hv[i] = silu(acc[0][mb][4 * g + i]) * acc[1][mb][4 * g + i];
-          uint2 pk = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) = pk;
+        for (int nb = 0; nb < 2; ++nb) {
+          const int n = tile.nt * 128 + wn * 64 + nb * 32 + nloc;
+          if (n < N) {
+            float hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + 2][mb][4 * g + i];
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
+                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          }
         }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = tile.nt * BNW + brow[nb] + nloc;
+        for (int nb = 0; nb < 4; ++nb) {
+          const int n = tile.nt * TW + wn * 128 + nb * 32 + nloc;
           if (n < N)
             *reinterpret_cast<float4*>(static_cast<float*>(Cv) + crow + n) =
                 make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
@@ -268,14 +343,15 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(
   }
 }
 
-}  // namespace
-
-// upper bound on sum_e ceil(M_e / BM) over the experts' row counts M_e
-static unsigned tile_grid(int rows, int E, int nN) {
+// upper bound on sum_e ceil(M_e / BM) over the experts' row counts M_e,
+// times the column tiles, rounded up to whole XCD rounds
+unsigned tile_grid(int rows, int E, int BM, int nN) {
   const long long max_mt = rows / BM + (rows < E ? rows : E);
   const long long g = max_mt * nN;
   return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds);
 }
+
+}  // namespace
 
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
@@ -287,7 +363,7 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
         static_cast<const float*>(w_up), ffn, d, static_cast<float*>(h));
     return launch_status();
   }
-  expert_gemm_bf16_kernel<true><<<tile_grid(rows, E, (ffn + 63) / 64), NT, 0, s>>>(
+  expert_gemm_bf16_kernel<true><<<tile_grid(rows, E, TM, (ffn + 127) / 128), TNT, 0, s>>>(
       static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
       static_cast<const bf16_t*>(w_up), ffn, d, h);
   return launch_status();
@@ -302,7 +378,7 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
         nullptr, d, ffn, y);
     return launch_status();
   }
-  expert_gemm_bf16_kernel<false><<<tile_grid(rows, E, (d + BNW - 1) / BNW), NT, 0, s>>>(
+  expert_gemm_bf16_kernel<false><<<tile_grid(rows, E, TM, (d + TW - 1) / TW), TNT, 0, s>>>(
       static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
       nullptr, d, ffn, y);
   return launch_status();
