@@ -112,11 +112,11 @@ def main():
     gu_flops = 4.0 * rows * w.d * w.ffn
     gu_bytes = touched * 2 * w.ffn * w.d * 2 + rows * w.d * 2 + rows * w.ffn * 2
     gu_s = stage_ms["gate_up"] / 1e3
-    if rows >= 4 * w.E * 32:   # enough rows per expert to be MFMA-bound
-        roof = {"kernel": "expert_gemm_bf16_kernel<gate_up>", "bound": "mfma",
+    if rows > 32 * w.E:   # tiled MFMA kernels (the library's own switch)
+        roof = {"kernel": "expert_gemm_bf16_kernel<true>", "bound": "mfma",
                 "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": "expert_gemm_bf16_kernel<gate_up>", "bound": "hbm",
+    else:                   # weight-streaming kernels
+        roof = {"kernel": "expert_stream_kernel<true>", "bound": "hbm",
                 "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["mean_ms"] = stage_ms["gate_up"]

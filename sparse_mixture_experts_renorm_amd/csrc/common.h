@@ -11,6 +11,7 @@ namespace moe {
 constexpr int kWave = 64;         // CDNA wavefront width
 constexpr int kMaxExperts = 256;  // library limit on E
 constexpr int kMaxTopK = 16;      // library limit on k
+constexpr int kMaxDownSplit = 4;  // most parts the down GEMM's reduction is cut into
 
 typedef uint16_t bf16_t;          // bfloat16 storage (bit pattern)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,7 +50,8 @@ struct Workspace {
   int32_t* sorted_token;  // [T*k]
   int32_t* inv_pos;       // [T*k]
   void* h;                // [T*k, ffn] in dt
-  float* y;               // [T*k, d] fp32
+  float* y;               // [kMaxDownSplit, T*k, d] fp32 partial sums of the down GEMM
+  int32_t* split;         // [1] number of partial sums in y
   size_t bytes;
 };
 
@@ -69,7 +71,8 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   w.sorted_token = reinterpret_cast<int32_t*>(take(tk * 4));
   w.inv_pos = reinterpret_cast<int32_t*>(take(tk * 4));
   w.h = take(tk * static_cast<size_t>(ffn) * es);
-  w.y = reinterpret_cast<float*>(take(tk * static_cast<size_t>(d) * 4));
+  w.y = reinterpret_cast<float*>(take(kMaxDownSplit * tk * static_cast<size_t>(d) * 4));
+  w.split = reinterpret_cast<int32_t*>(take(4));
   w.bytes = off;
   return w;
 }
@@ -87,8 +90,17 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
                           int k, moe_dtype dt, void* h, hipStream_t s);
 moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down, int T, int d,
-                       int ffn, int E, int k, moe_dtype dt, float* y, hipStream_t s);
-moe_status launch_combine(const float* y, const int32_t* inv_pos, const float* topk_w, int T,
-                          int d, int k, void* out, moe_dtype out_dt, hipStream_t s);
+                       int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
+                       hipStream_t s);
+moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
+                                 const int32_t* offsets, const void* w_gate, const void* w_up,
+                                 int d, int ffn, int E, void* h, hipStream_t s);
+moe_status launch_down_stream(const void* h, const int32_t* offsets, const void* w_down, int d,
+                              int ffn, int E, float* y, int32_t* split, hipStream_t s);
+// Few rows per expert: the weight-streaming kernels replace the tiled ones.
+inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
+moe_status launch_combine(const float* y, const int32_t* split, const int32_t* inv_pos,
+                          const float* topk_w, int T, int d, int k, void* out, moe_dtype out_dt,
+                          hipStream_t s);
 
 }  // namespace moe

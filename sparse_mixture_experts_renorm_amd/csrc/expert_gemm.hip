@@ -45,31 +45,51 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int GN = 8;     // column tiles per schedule group
+constexpr int kMinSplitSteps = 48;
 
 struct Tile {
   int e, row0, rows, nt;
+  int ks, S;  // split of the reduction dimension: this tile computes part ks of S
 };
 
 // Map this workgroup to a tile of BM rows; returns false if it has none.
+// With max_split > 1 the reduction dimension may be cut into S <= max_split
+// parts, each a separate tile whose partial result goes to its own output
+// slice; S is chosen from the real tile count to minimise the number of
+// rounds on n_cu CUs, counted in units of a whole tile, with at least
+// kMinSplitSteps of the nk reduction steps in every part (shorter parts
+// would spend more on the extra partial sums than they save).
 template <int BM>
-__device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, Tile* out) {
-  __shared__ int s_tile[4];
+__device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
+                         int n_cu, int nk, Tile* out) {
+  __shared__ int s_tile[6];
   if (threadIdx.x == 0) {
-    int total = 0;
+    int base = 0;
     for (int e = 0; e < E; ++e) {
       const int m = offsets[e + 1] - offsets[e];
-      total += ((m + BM - 1) / BM) * nN;
+      base += ((m + BM - 1) / BM) * nN;
     }
+    int S = 1, best_rounds = (base + n_cu - 1) / n_cu;  // rounds of S-tiles
+    for (int c = 2; c <= max_split && c * kMinSplitSteps <= nk; ++c) {
+      const int rounds = (base * c + n_cu - 1) / n_cu;
+      if (rounds * S < best_rounds * c) {  // rounds/c < best_rounds/S
+        S = c;
+        best_rounds = rounds;
+      }
+    }
+    const int total = base * S;
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
     int L = xcd * per_xcd + slot;
-    int res_e = -1, res_m = 0, res_n = 0;
+    int res_e = -1, res_m = 0, res_n = 0, res_s = 0;
     if (slot < per_xcd && L < total) {
       for (int e = 0; e < E; ++e) {
         const int m = offsets[e + 1] - offsets[e];
         const int mt = (m + BM - 1) / BM;
-        const int te = mt * nN;
-        if (L < te) {
+        const int te = mt * nN;  // tiles of one split of expert e
+        if (L < te * S) {
+          res_s = L / te;
+          L -= res_s * te;
           const int g = L / (mt * GN);
           const int r = L % (mt * GN);
           const int gn = min(GN, nN - g * GN);
@@ -78,10 +98,12 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, Til
           res_n = g * GN + r % gn;
           break;
         }
-        L -= te;
+        L -= te * S;
       }
     }
     s_tile[0] = res_e;
+    s_tile[4] = res_s;
+    s_tile[5] = S;
     if (res_e >= 0) {
       const int m = offsets[res_e + 1] - offsets[res_e];
       s_tile[1] = offsets[res_e] + res_m * BM;
@@ -90,11 +112,13 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, Til
     }
   }
   __syncthreads();
+  out->S = s_tile[5];
   if (s_tile[0] < 0) return false;
   out->e = s_tile[0];
   out->row0 = s_tile[1];
   out->rows = s_tile[2];
   out->nt = s_tile[3];
+  out->ks = s_tile[4];
   return true;
 }
 
@@ -115,13 +139,16 @@ constexpr int STAGE = TM * TK * 2;  // bytes per operand and stage (32 KB)
 constexpr int IPW = 8;         // 1 KB load instructions per wave, per operand and stage
 
 // GATE_UP: A = x gathered by sorted_token, weights = [w_gate; w_up], C = h (bf16).
-// !GATE_UP: A = h (rows in order), weights = w_down, C = y (fp32).
+// !GATE_UP: A = h (rows in order), weights = w_down, C = y (fp32); the
+// reduction may be split (see map_tile): part ks writes C + ks * c_split,
+// and workgroup 0 stores the split count S in *split_out.
 template <bool GATE_UP>
 __global__ __launch_bounds__(TNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
                              const int32_t* __restrict__ offsets, int E,
                              const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
-                             int K, void* __restrict__ Cv) {
+                             int K, void* __restrict__ Cv, int max_split, int n_cu,
+                             size_t c_split, int32_t* __restrict__ split_out) {
   // One LDS object per stage and operand. They must be distinct objects: the
   // compiler then sees that the memory-to-LDS loads of the next stage cannot
   // alias the fragment reads of the current one, and does not make those
@@ -136,7 +163,12 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   };
   const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
-  if (!map_tile<TM>(offsets, E, nN, &tile)) return;
+  const int nk = (K + TK - 1) / TK;
+  const bool have = map_tile<TM>(offsets, E, nN, max_split, n_cu, nk, &tile);
+  if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
+  if (!have) return;
+  // reduction steps [kbeg, kend) of this tile
+  const int kbeg = tile.ks * nk / tile.S, kend = (tile.ks + 1) * nk / tile.S;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -181,7 +213,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   auto issue_one = [&](int kt, int st, int j) {
     const int k0 = kt * TK;
     const int jj = j % IPW;
-    const bool kin = k0 + kchunk[jj] * 8 < K;
+    const bool kin = kt < kend && k0 + kchunk[jj] * 8 < K;
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
     if (j < IPW)
       load_lds16(kin ? a_base + (a_off[jj] + kb) : zero, buf(st, 0) + (wave * IPW + jj) * 1024);
@@ -251,19 +283,18 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // Before step kt is computed its loads must have landed in LDS (each wave
   // waits for its own); the barrier then makes every wave's loads visible
   // and guarantees that the other stage, overwritten during step kt, is no
-  // longer read. The step count is rounded up to even; a step past K loads
-  // zeros.
-  const int nk = (K + TK - 1) / TK;
-  const int nk2 = (nk + 1) & ~1;
+  // longer read. The step count is rounded up to even; a step past the
+  // tile's range loads zeros.
+  const int kend2 = kbeg + ((kend - kbeg + 1) & ~1);
 #pragma unroll
-  for (int j = 0; j < 2 * IPW; ++j) issue_one(0, 0, j);
-  for (int kt0 = 0; kt0 < nk2; kt0 += 2) {
+  for (int j = 0; j < 2 * IPW; ++j) issue_one(kbeg, 0, j);
+  for (int kt0 = kbeg; kt0 < kend2; kt0 += 2) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int kt = kt0 + r;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      step(kt, r, kt + 1 < nk2);
+      step(kt, r, kt + 1 < kend2);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -296,7 +327,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
         for (int nb = 0; nb < 4; ++nb) {
           const int n = tile.nt * TW + wn * 128 + nb * 32 + nloc;
           if (n < N)
-            *reinterpret_cast<float4*>(static_cast<float*>(Cv) + crow + n) =
+            *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
                 make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
                             acc[nb][mb][4 * g + 3]);
         }
@@ -321,9 +352,11 @@ template <bool GATE_UP>
 __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(
     const float* __restrict__ A, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, int E, const float* __restrict__ B0,
-    const float* __restrict__ B1, int N, int K, float* __restrict__ C) {
+    const float* __restrict__ B1, int N, int K, float* __restrict__ C,
+    int32_t* __restrict__ split_out) {
   const int r = blockIdx.x;
   const int n = blockIdx.y * 256 + threadIdx.x;
+  if (!GATE_UP && split_out && r == 0 && n == 0) *split_out = 1;
   if (r >= offsets[E] || n >= N) return;
   const int e = expert_of_row(offsets, E, r);
   const float* a = A + static_cast<size_t>(GATE_UP ? sorted_token[r] : r) * K;
@@ -344,11 +377,19 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(
 }
 
 // upper bound on sum_e ceil(M_e / BM) over the experts' row counts M_e,
-// times the column tiles, rounded up to whole XCD rounds
-unsigned tile_grid(int rows, int E, int BM, int nN) {
+// times the column tiles and splits, rounded up to whole XCD rounds
+unsigned tile_grid(int rows, int E, int BM, int nN, int splits) {
   const long long max_mt = rows / BM + (rows < E ? rows : E);
-  const long long g = max_mt * nN;
+  const long long g = max_mt * nN * splits;
   return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds);
+}
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  return n;
 }
 
 }  // namespace
@@ -360,27 +401,32 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
   if (dt == MOE_F32) {
     expert_gemm_f32_kernel<true><<<dim3(rows, (ffn + 255) / 256), 256, 0, s>>>(
         static_cast<const float*>(x), sorted_token, offsets, E, static_cast<const float*>(w_gate),
-        static_cast<const float*>(w_up), ffn, d, static_cast<float*>(h));
+        static_cast<const float*>(w_up), ffn, d, static_cast<float*>(h), nullptr);
     return launch_status();
   }
-  expert_gemm_bf16_kernel<true><<<tile_grid(rows, E, TM, (ffn + 127) / 128), TNT, 0, s>>>(
+  if (use_stream_path(rows, E))
+    return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, h, s);
+  expert_gemm_bf16_kernel<true><<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), TNT, 0, s>>>(
       static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
-      static_cast<const bf16_t*>(w_up), ffn, d, h);
+      static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
   return launch_status();
 }
 
 moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down, int T, int d,
-                       int ffn, int E, int k, moe_dtype dt, float* y, hipStream_t s) {
+                       int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
+                       hipStream_t s) {
   const int rows = T * k;
   if (dt == MOE_F32) {
     expert_gemm_f32_kernel<false><<<dim3(rows, (d + 255) / 256), 256, 0, s>>>(
         static_cast<const float*>(h), nullptr, offsets, E, static_cast<const float*>(w_down),
-        nullptr, d, ffn, y);
+        nullptr, d, ffn, y, split);
     return launch_status();
   }
-  expert_gemm_bf16_kernel<false><<<tile_grid(rows, E, TM, (d + TW - 1) / TW), TNT, 0, s>>>(
+  if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, y, split, s);
+  expert_gemm_bf16_kernel<false><<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), TNT,
+                                   0, s>>>(
       static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
-      nullptr, d, ffn, y);
+      nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
   return launch_status();
 }
 

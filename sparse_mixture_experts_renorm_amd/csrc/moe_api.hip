@@ -105,10 +105,10 @@ static moe_status run_experts(const void* x, const int32_t* topk_idx, const floa
                       stream);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], stream);
-  st = launch_down(ws.h, ws.offsets, w_down, T, d, ffn, E, k, dt, ws.y, stream);
+  st = launch_down(ws.h, ws.offsets, w_down, T, d, ffn, E, k, dt, ws.y, ws.split, stream);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[4], stream);
-  st = launch_combine(ws.y, ws.inv_pos, topk_w, T, d, k, out, out_dt, stream);
+  st = launch_combine(ws.y, ws.split, ws.inv_pos, topk_w, T, d, k, out, out_dt, stream);
   if (ev) hipEventRecord(ev[5], stream);
   return st;
 }

@@ -110,6 +110,11 @@ EXPERT_SHAPES = [
     (1, 64, 64, 4, 2, "bf16", "random"),
     (40, 64, 96, 1, 1, "bf16", "random"),
     (90, 96, 112, 5, 5, "bf16", "random"),       # k = E
+    # at most 32 rows per expert on average: the weight-streaming kernels
+    (40, 272, 336, 4, 2, "bf16", "random"),      # ragged K tails on both passes
+    (60, 128, 192, 4, 2, "bf16", "all_same"),    # 60 rows on experts 0 and 1 (two row blocks)
+    (16, 64, 96, 8, 1, "bf16", "one_heavy"),     # k = 1, every token on expert 7
+    (32, 4096, 14336, 8, 2, "bf16", "random"),   # decode shape
 ]
 
 
