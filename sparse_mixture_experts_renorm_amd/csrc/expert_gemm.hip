@@ -134,16 +134,17 @@ __device__ __forceinline__ void load_lds16(const void* g, char* lds_chunk_base) 
 constexpr int TM = 256;        // permuted rows per tile
 constexpr int TW = 256;        // weight rows per tile
 constexpr int TK = 64;         // reduction step (elements); one LDS row = 128 bytes
-constexpr int TNT = 256;       // threads per workgroup
 constexpr int STAGE = TM * TK * 2;  // bytes per operand and stage (32 KB)
-constexpr int IPW = 8;         // 1 KB load instructions per wave, per operand and stage
 
 // GATE_UP: A = x gathered by sorted_token, weights = [w_gate; w_up], C = h (bf16).
 // !GATE_UP: A = h (rows in order), weights = w_down, C = y (fp32); the
 // reduction may be split (see map_tile): part ks writes C + ks * c_split,
 // and workgroup 0 stores the split count S in *split_out.
-template <bool GATE_UP>
-__global__ __launch_bounds__(TNT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW waves per workgroup: 4 (wave tile 128 x 128, one wave per SIMD) or 8
+// (wave tile 128 x 64, two waves per SIMD, so one wave's MFMAs run while the
+// other waits to issue its loads).
+template <bool GATE_UP, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
                              const int32_t* __restrict__ offsets, int E,
                              const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
@@ -170,16 +171,19 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // reduction steps [kbeg, kend) of this tile
   const int kbeg = tile.ks * nk / tile.S, kend = (tile.ks + 1) * nk / tile.S;
 
+  constexpr int IPW = 32 / NW;   // 1 KB load instructions per wave, per operand and stage
+  constexpr int WN = NW / 2;     // waves along the weight rows
+  constexpr int NBW = 8 / WN;    // 32-row weight blocks per wave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   // ---- direct-load sources. Per stage each operand is 256 rows x 128 bytes,
   // loaded by 1 KB instructions of 8 rows; wave w issues instructions
   // 8w .. 8w+7. In instruction q lane l writes row r = q*8 + l/8, slot l%8,
   // which holds chunk (l%8) ^ ((r >> 1) & 7).
   // Sources are 32-bit byte offsets from one base per operand. Rows past the
-  // tile's valid rows (or past N) repeat a valid row: their products are
+  // tile's valid rows (or past N) repeat valid rows: their products are
   // computed but never stored. Chunks past K read the zero page.
   // Tile row r of the weight operand: gate/up rows 0-127 are gate rows
   // n0 .. n0+127, rows 128-255 the same rows of up; down rows are n0 + r.
@@ -187,7 +191,9 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const char* a_base = reinterpret_cast<const char*>(A);
   const size_t wexp = static_cast<size_t>(tile.e) * N * K * 2;
   auto a_row_off = [&](int r) -> uint32_t {
-    const int rr = r < tile.rows ? r : 0;
+    // past the valid rows, spread the repeats over all valid rows (one
+    // repeated row for a whole load instruction would hit one cache line)
+    const int rr = r < tile.rows ? r : r % tile.rows;
     const uint32_t arow = GATE_UP ? static_cast<uint32_t>(sorted_token[tile.row0 + rr])
                                   : static_cast<uint32_t>(tile.row0 + rr);
     return arow * static_cast<uint32_t>(K) * 2u;
@@ -213,7 +219,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   auto issue_one = [&](int kt, int st, int j) {
     const int k0 = kt * TK;
     const int jj = j % IPW;
-    const bool kin = kt < kend && k0 + kchunk[jj] * 8 < K;
+    const bool kin = k0 + kchunk[jj] * 8 < K;
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
     if (j < IPW)
       load_lds16(kin ? a_base + (a_off[jj] + kb) : zero, buf(st, 0) + (wave * IPW + jj) * 1024);
@@ -223,17 +229,21 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // ---- fragment reads: row R's chunk c is at R*128 + ((c ^ ((R >> 1) & 7)) << 4);
   // every row this lane reads has R % 32 == lane % 32.
   const int xr = ((lane & 31) >> 1) & 7, half = lane >> 5;
-  int fa_off[4], fb_off[4];
+  // weight blocks of this wave: gate/up: NBW/2 gate blocks, then the same
+  // rows of up (tile rows + 128); down: NBW consecutive blocks
+  int fa_off[4], fb_off[NBW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa_off[i] = (wm * 128 + i * 32 + (lane & 31)) * 128;
-    const int brow = GATE_UP ? (i >> 1) * 128 + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+  for (int i = 0; i < 4; ++i) fa_off[i] = (wm * 128 + i * 32 + (lane & 31)) * 128;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int brow = GATE_UP ? (i / (NBW / 2)) * 128 + wn * (NBW / 2) * 32 + (i % (NBW / 2)) * 32
+                             : wn * NBW * 32 + i * 32;
     fb_off[i] = (brow + (lane & 31)) * 128;
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[NBW][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < NBW; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -244,11 +254,11 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(buf(st, 0) + fa_off[i] + slot);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fb[i] = *reinterpret_cast<const bf16x8*>(buf(st, 1) + fb_off[i] + slot);
+    for (int i = 0; i < NBW; ++i) fb[i] = *reinterpret_cast<const bf16x8*>(buf(st, 1) + fb_off[i] + slot);
   };
   auto mma16 = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
@@ -262,7 +272,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 #pragma unroll
       for (int j = 0; j < 2 * IPW; ++j) issue_one(kt + 1, st ^ 1, j);
     }
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][4], fb[2][NBW];
     read_frags(st, 0, fa[0], fb[0]);
 #pragma unroll
     for (int s = 0; s < TK / 16; ++s) {
@@ -270,12 +280,13 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
       if (s + 1 < TK / 16) read_frags(st, s + 1, fa[cur ^ 1], fb[cur ^ 1]);
       mma16(fa[cur], fb[cur]);
       if (s + 1 < TK / 16) {
+        // one fragment read after each of the first 4 + NBW MFMAs
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4 + NBW; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 fragment read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBW - 4 - NBW, 0);
       }
     }
   };
@@ -283,24 +294,32 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // Before step kt is computed its loads must have landed in LDS (each wave
   // waits for its own); the barrier then makes every wave's loads visible
   // and guarantees that the other stage, overwritten during step kt, is no
-  // longer read. The step count is rounded up to even; a step past the
-  // tile's range loads zeros.
-  const int kend2 = kbeg + ((kend - kbeg + 1) & ~1);
+  // longer read. Steps go in pairs (stage 0, stage 1); an odd last step runs
+  // on stage 0 and issues nothing.
+  const int nsteps = kend - kbeg;
+  if (nsteps > 0) {
 #pragma unroll
-  for (int j = 0; j < 2 * IPW; ++j) issue_one(kbeg, 0, j);
-  for (int kt0 = kbeg; kt0 < kend2; kt0 += 2) {
+    for (int j = 0; j < 2 * IPW; ++j) issue_one(kbeg, 0, j);
+  }
+  for (int p = 0; p + 1 < nsteps; p += 2) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int kt = kt0 + r;
+      const int kt = kbeg + p + r;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      step(kt, r, kt + 1 < kend2);
+      step(kt, r, kt + 1 < kend);
     }
+  }
+  if (nsteps & 1) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    step(kend - 1, 0, false);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue. acc[nb][mb] element i: token row wm*128 + mb*32 + lane%32,
-  // weight-tile row (block nb) + 8*(i/4) + 4*(lane/32) + i%4.
+  // weight-tile row (block nb) + 8*(i/4) + 4*(lane/32) + i%4. Gate block nb
+  // pairs with up block nb + NBW/2.
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int m = wm * 128 + mb * 32 + (lane & 31);
@@ -311,21 +330,21 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
       const int nloc = 8 * g + 4 * half;
       if (GATE_UP) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = tile.nt * 128 + wn * 64 + nb * 32 + nloc;
+        for (int nb = 0; nb < NBW / 2; ++nb) {
+          const int n = tile.nt * 128 + wn * (NBW / 2) * 32 + nb * 32 + nloc;
           if (n < N) {
             float hv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + 2][mb][4 * g + i];
+              hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + NBW / 2][mb][4 * g + i];
             *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
                 make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
           }
         }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int n = tile.nt * TW + wn * 128 + nb * 32 + nloc;
+        for (int nb = 0; nb < NBW; ++nb) {
+          const int n = tile.nt * TW + wn * NBW * 32 + nb * 32 + nloc;
           if (n < N)
             *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
                 make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
@@ -378,6 +397,11 @@ __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(
 
 // upper bound on sum_e ceil(M_e / BM) over the experts' row counts M_e,
 // times the column tiles and splits, rounded up to whole XCD rounds
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+constexpr int kWaves = MOE_GEMM_WAVES;
+
 unsigned tile_grid(int rows, int E, int BM, int nN, int splits) {
   const long long max_mt = rows / BM + (rows < E ? rows : E);
   const long long g = max_mt * nN * splits;
@@ -406,7 +430,7 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
   }
   if (use_stream_path(rows, E))
     return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, h, s);
-  expert_gemm_bf16_kernel<true><<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), TNT, 0, s>>>(
+  expert_gemm_bf16_kernel<true, kWaves><<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), kWaves * 64, 0, s>>>(
       static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
       static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
   return launch_status();
@@ -423,7 +447,7 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
     return launch_status();
   }
   if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, y, split, s);
-  expert_gemm_bf16_kernel<false><<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), TNT,
+  expert_gemm_bf16_kernel<false, kWaves><<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64,
                                    0, s>>>(
       static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
       nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
