@@ -94,9 +94,9 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
                        hipStream_t s);
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
-                                 int d, int ffn, int E, void* h, hipStream_t s);
+                                 int d, int ffn, int E, int rows, void* h, hipStream_t s);
 moe_status launch_down_stream(const void* h, const int32_t* offsets, const void* w_down, int d,
-                              int ffn, int E, float* y, int32_t* split, hipStream_t s);
+                              int ffn, int E, int rows, float* y, int32_t* split, hipStream_t s);
 // Few rows per expert: the weight-streaming kernels replace the tiled ones.
 inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
 moe_status launch_combine(const float* y, const int32_t* split, const int32_t* inv_pos,

@@ -429,7 +429,7 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
     return launch_status();
   }
   if (use_stream_path(rows, E))
-    return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, h, s);
+    return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows, h, s);
   expert_gemm_bf16_kernel<true, kWaves><<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), kWaves * 64, 0, s>>>(
       static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
       static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
@@ -446,7 +446,7 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
         nullptr, d, ffn, y, split);
     return launch_status();
   }
-  if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, y, split, s);
+  if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, rows, y, split, s);
   expert_gemm_bf16_kernel<false, kWaves><<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64,
                                    0, s>>>(
       static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),

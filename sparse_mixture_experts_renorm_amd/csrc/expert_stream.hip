@@ -4,17 +4,22 @@
 // SiLU(X W_g^T) * (X W_u^T), y = h W_d^T over each expert's permuted rows),
 // for the case where every expert holds only a handful of rows: the time is
 // then the streaming of the expert weights from HBM, and each weight byte is
-// used by at most a few MFMAs. Layout:
-//   - one wave owns 32 weight rows (gate/up: 32 gate rows and the same 32
-//     up rows) of one expert and all of that expert's rows, in blocks of
-//     32 (v_mfma_f32_32x32x16_bf16, weights as the first operand);
-//   - weights go straight from memory to registers, no LDS: per 64-wide
-//     reduction chunk lane l loads 64 contiguous bytes of weight row l%32
-//     (half l/32 of the 128-byte chunk) as four 16-byte loads, and MFMA i of
-//     the chunk uses load i. The token operand is loaded with the same
-//     lane -> reduction-index map, so every product pairs equal indices;
-//   - chunks are prefetched DEPTH deep in registers so each wave keeps
-//     DEPTH x 8 KB of weights in flight;
+// used by a few MFMAs at most. Layout:
+//   - v_mfma_f32_16x16x32_bf16 with the weights as the first operand: lane l
+//     supplies weight row l%16 and the 8 reduction indices 8*(l/16).. of a
+//     32-wide step, so the four lanes of a row read 64 contiguous bytes and
+//     one load instruction covers 16 whole 64-byte pieces. (Loads whose
+//     64-byte pieces are split over several instructions are fetched
+//     several times and cap the stream well below the HBM rate.) The token
+//     operand uses the same lane -> reduction-index map;
+//   - one wave owns 16*RB weight rows of one expert (gate/up: those rows of
+//     both matrices) and NB blocks of 16 token rows, accumulating all of
+//     them in one pass over the weights; experts with more rows take more
+//     passes;
+//   - weights go straight from memory to registers, DEPTH 64-wide reduction
+//     chunks ahead;
+//   - the down GEMM may cut the reduction into S parts (blockIdx.z), each
+//     writing its own fp32 partial; the combine sums the parts in order;
 //   - experts without rows exit at once, so their weights are never read.
 // Token rows past an expert's count repeat a valid row; their results are
 // never stored.
@@ -23,139 +28,227 @@
 namespace moe {
 namespace {
 
-constexpr int SW = 4;       // waves per workgroup
-constexpr int DEPTH = 3;    // reduction chunks in flight per wave
+constexpr int SW = 4;     // waves per workgroup
+constexpr int DEPTH = 3;  // reduction chunks in flight per wave
 
 __device__ __forceinline__ uint4 ld16(const bf16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// Grid: (ceil(N / (32 * SW)), E). GATE_UP: A = x gathered by sorted_token,
-// weight rows from w_gate and w_up, C = h (bf16). !GATE_UP: A = h rows,
-// weights w_down, C = y (fp32).
-template <bool GATE_UP>
-__global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
-    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ B0,
-    const bf16_t* __restrict__ B1, int N, int K, void* __restrict__ Cv,
-    int32_t* __restrict__ split_out) {
-  if (!GATE_UP && split_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
-    *split_out = 1;
-  const int e = blockIdx.y;
-  const int row0 = offsets[e], rows = offsets[e + 1] - row0;
-  if (rows == 0) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * SW + wave) * 32;
-  if (n0 >= N) return;
-  const int half = lane >> 5, r32 = lane & 31;
-  const int nrow = min(n0 + r32, N - 1);
-  const size_t wrow = (static_cast<size_t>(e) * N + nrow) * K;
-  const bf16_t* wg = B0 + wrow + half * 32;
-  const bf16_t* wu = GATE_UP ? B1 + wrow + half * 32 : nullptr;
-  const int nchunks = K / 64;   // K is a multiple of 16; the tail is handled below
-  const int ktail = K - nchunks * 64;
+// lane L takes the 16 bytes lane 4*(L%16) + L/16 loaded (byte address xa)
+__device__ __forceinline__ uint4 xpose(uint4 v, int xa) {
+  return make_uint4(__builtin_amdgcn_ds_bpermute(xa, static_cast<int>(v.x)),
+                    __builtin_amdgcn_ds_bpermute(xa, static_cast<int>(v.y)),
+                    __builtin_amdgcn_ds_bpermute(xa, static_cast<int>(v.z)),
+                    __builtin_amdgcn_ds_bpermute(xa, static_cast<int>(v.w)));
+}
 
-  for (int mb = 0; mb < rows; mb += 32) {
-    const int m = mb + r32 < rows ? mb + r32 : mb;  // repeat a valid row past the end
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One pass over reduction range [kbeg, kend) (kbeg a multiple of 64) for
+// token rows mb .. mb + 16*NB of expert rows starting at row0.
+template <bool GATE_UP, int RB, int NB>
+__device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
+                                            const int32_t* __restrict__ sorted_token,
+                                            const bf16_t* const (&wg)[RB],
+                                            const bf16_t* const (&wu)[RB], int row0, int rows,
+                                            int mb, int n0, int N, int K, int kbeg, int kend,
+                                            void* __restrict__ Cv, int lane) {
+  const int r16 = lane & 15, q = lane >> 4;
+  const int lr = lane >> 2, lp = lane & 3;  // load layout: row lane/4, piece lane%4
+  const int xa = 4 * (4 * r16 + q);
+  const bf16_t* ap[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    int m = mb + t * 16 + lr;
+    m = m < rows ? m : mb;  // repeat a valid row past the end
     const size_t arow = GATE_UP ? static_cast<size_t>(sorted_token[row0 + m])
                                 : static_cast<size_t>(row0 + m);
-    const bf16_t* ap = A + arow * K + half * 32;
+    ap[t] = A + arow * K + lp * 8;
+  }
+  f32x4 accg[RB][NB], accu[RB][NB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accg[r][t][i] = accu[r][t][i] = 0.f;
 
-    f32x16 acc_g, acc_u;
+  // chunk = two 32-wide steps; slot s holds one chunk
+  uint4 bw[DEPTH][RB][2], bu[DEPTH][RB][2], ba[DEPTH][NB][2];
+  auto load = [&](int k0, int s) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc_g[i] = acc_u[i] = 0.f;
-
-    uint4 bw[DEPTH][4], bu[DEPTH][4], ba[DEPTH][4];
-    auto load = [&](int c, int slot) {
-      const int k0 = c * 64;
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bw[slot][i] = ld16(wg + k0 + i * 8);
-        if (GATE_UP) bu[slot][i] = ld16(wu + k0 + i * 8);
-        ba[slot][i] = ld16(ap + k0 + i * 8);
+      for (int r = 0; r < RB; ++r) {
+        bw[s][r][j] = ld16(wg[r] + k0 + 32 * j);
+        if (GATE_UP) bu[s][r][j] = ld16(wu[r] + k0 + 32 * j);
       }
-    };
-    auto mma = [&](int slot) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, ba[slot][i]);
-        acc_g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bw[slot][i]), a,
-                                                        acc_g, 0, 0, 0);
-        if (GATE_UP)
-          acc_u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bu[slot][i]),
-                                                          a, acc_u, 0, 0, 0);
-      }
-    };
-#pragma unroll
-    for (int c = 0; c < DEPTH; ++c)
-      if (c < nchunks) load(c, c);
-    int c = 0;
-    for (; c + DEPTH <= nchunks; c += DEPTH) {
-#pragma unroll
-      for (int s = 0; s < DEPTH; ++s) {
-        mma(s);
-        if (c + s + DEPTH < nchunks) load(c + s + DEPTH, s);
-      }
+      for (int t = 0; t < NB; ++t) ba[s][t][j] = ld16(ap[t] + k0 + 32 * j);
     }
+  };
+  auto mma = [&](int s) {
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s)
-      if (c + s < nchunks) mma(s);
-    if (ktail) {
-      // last K % 64 elements, in 16-wide steps: lanes of half h take the
-      // 8 elements at 16*i + 8*h, with the same map for both operands
-      const int k0 = nchunks * 64;
-      for (int i = 0; i < ktail / 16; ++i) {
-        const int kk = k0 + i * 16 + half * 8 - half * 32;  // pointers carry + half*32
-        const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(ap + kk));
-        acc_g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(wg + kk)),
-                                                        a, acc_g, 0, 0, 0);
-        if (GATE_UP)
-          acc_u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(wu + kk)),
-                                                          a, acc_u, 0, 0, 0);
-      }
-    }
-
-    // acc element i: weight row n0 + 8*(i/4) + 4*half + i%4, token row mb + lane%32
-    const int mt = mb + r32;
-    if (mt < rows) {
-      const size_t crow = static_cast<size_t>(row0 + mt) * N;
+    for (int j = 0; j < 2; ++j) {
+      uint4 a[NB];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + 8 * g + 4 * half;
-        if (n >= N) continue;
+      for (int t = 0; t < NB; ++t) a[t] = xpose(ba[s][t][j], xa);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const uint4 g = xpose(bw[s][r][j], xa);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) accg[r][t] = mfma16(g, a[t], accg[r][t]);
         if (GATE_UP) {
-          float hv[4];
+          const uint4 u = xpose(bu[s][r][j], xa);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) hv[i] = silu(acc_g[4 * g + i]) * acc_u[4 * g + i];
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
-              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(Cv) + crow + n) =
-              make_float4(acc_g[4 * g], acc_g[4 * g + 1], acc_g[4 * g + 2], acc_g[4 * g + 3]);
+          for (int t = 0; t < NB; ++t) accu[r][t] = mfma16(u, a[t], accu[r][t]);
         }
+      }
+    }
+  };
+  const int nchunks = (kend - kbeg) / 64;
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s)
+    if (s < nchunks) load(kbeg + 64 * s, s);
+  int c = 0;
+  for (; c + DEPTH <= nchunks; c += DEPTH) {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+      mma(s);
+      if (c + s + DEPTH < nchunks) load(kbeg + 64 * (c + s + DEPTH), s);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s)
+    if (c + s < nchunks) mma(s);
+  // reduction tail (kend - kbeg not a multiple of 64): 32-wide steps whose
+  // 8-element groups past kend read nothing and add zero (K % 8 == 0)
+  for (int k0 = kbeg + 64 * nchunks; k0 < kend; k0 += 32) {
+    const bool in = k0 + lp * 8 < kend;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    uint4 a[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) a[t] = xpose(in ? ld16(ap[t] + k0) : z, xa);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const uint4 g = xpose(in ? ld16(wg[r] + k0) : z, xa);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) accg[r][t] = mfma16(g, a[t], accg[r][t]);
+      if (GATE_UP) {
+        const uint4 u = xpose(in ? ld16(wu[r] + k0) : z, xa);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) accu[r][t] = mfma16(u, a[t], accu[r][t]);
+      }
+    }
+  }
+
+  // acc[r][t] element i: weight row n0 + 16r + 4q + i, token row mb + 16t + r16
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const int m = mb + t * 16 + r16;
+    if (m >= rows) continue;
+    const size_t crow = static_cast<size_t>(row0 + m) * N;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int n = n0 + 16 * r + 4 * q;
+      if (n >= N) continue;  // N % 16 == 0: all four columns or none
+      if (GATE_UP) {
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = silu(accg[r][t][i]) * accu[r][t][i];
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
+            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(Cv) + crow + n) =
+            make_float4(accg[r][t][0], accg[r][t][1], accg[r][t][2], accg[r][t][3]);
       }
     }
   }
 }
 
+// Grid: (ceil(N / (16 * RB * SW)), E, S). GATE_UP: A = x gathered by
+// sorted_token, weight rows from w_gate and w_up, C = h (bf16). !GATE_UP:
+// A = h rows, weights w_down, C = y (fp32), part z at C + z * c_split.
+template <bool GATE_UP, int RB, int NB>
+__global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
+    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ B0,
+    const bf16_t* __restrict__ B1, int N, int K, void* __restrict__ Cv, size_t c_split,
+    int32_t* __restrict__ split_out) {
+  const int S = gridDim.z, z = blockIdx.z;
+  if (!GATE_UP && split_out && blockIdx.x == 0 && blockIdx.y == 0 && z == 0 && threadIdx.x == 0)
+    *split_out = S;
+  const int e = blockIdx.y;
+  const int row0 = offsets[e], rows = offsets[e + 1] - row0;
+  if (rows == 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * SW + wave) * 16 * RB;
+  if (n0 >= N) return;
+  // reduction part z: whole 64-wide chunks, the tail with the last part
+  const int nch = K / 64, per = nch / S, extra = nch % S;
+  const int kbeg = 64 * (z * per + min(z, extra));
+  const int kend = z == S - 1 ? K : kbeg + 64 * (per + (z < extra));
+  const int lr = lane >> 2, lp = lane & 3;
+  const bf16_t* wg[RB];
+  const bf16_t* wu[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int nrow = min(n0 + 16 * r + lr, N - 1);
+    const size_t wrow = (static_cast<size_t>(e) * N + nrow) * K + lp * 8;
+    wg[r] = B0 + wrow;
+    wu[r] = GATE_UP ? B1 + wrow : nullptr;
+  }
+  void* C = GATE_UP ? Cv : static_cast<void*>(static_cast<float*>(Cv) + z * c_split);
+  for (int mb = 0; mb < rows; mb += 16 * NB)
+    stream_pass<GATE_UP, RB, NB>(A, sorted_token, wg, wu, row0, rows, mb, n0, N, K, kbeg, kend, C,
+                             lane);
+}
+
+// 16-row token blocks per pass: enough for the average expert of the batch.
+inline int token_blocks(int rows, int E) { return rows <= 16 * E ? 1 : 2; }
+
+// Gate/up takes one 16-row weight block per wave (more waves for the
+// larger grid), down two (the grid is cut along the reduction instead).
+constexpr int kRbGateUp = 1, kRbDown = 2;
+
 }  // namespace
 
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
-                                 int d, int ffn, int E, void* h, hipStream_t s) {
-  dim3 grid((ffn + 32 * SW - 1) / (32 * SW), E);
-  expert_stream_kernel<true><<<grid, SW * 64, 0, s>>>(
-      static_cast<const bf16_t*>(x), sorted_token, offsets, static_cast<const bf16_t*>(w_gate),
-      static_cast<const bf16_t*>(w_up), ffn, d, h, nullptr);
+                                 int d, int ffn, int E, int rows, void* h, hipStream_t s) {
+  constexpr int RB = kRbGateUp;
+  dim3 grid((ffn + 16 * RB * SW - 1) / (16 * RB * SW), E, 1);
+  auto run = [&](auto kern) {
+    kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(x), sorted_token, offsets,
+                                  static_cast<const bf16_t*>(w_gate),
+                                  static_cast<const bf16_t*>(w_up), ffn, d, h, size_t(0), nullptr);
+  };
+  if (token_blocks(rows, E) == 1) run(expert_stream_kernel<true, RB, 1>);
+  else run(expert_stream_kernel<true, RB, 2>);
   return launch_status();
 }
 
 moe_status launch_down_stream(const void* h, const int32_t* offsets, const void* w_down, int d,
-                              int ffn, int E, float* y, int32_t* split, hipStream_t s) {
-  dim3 grid((d + 32 * SW - 1) / (32 * SW), E);
-  expert_stream_kernel<false><<<grid, SW * 64, 0, s>>>(
-      static_cast<const bf16_t*>(h), nullptr, offsets, static_cast<const bf16_t*>(w_down), nullptr,
-      d, ffn, y, split);
+                              int ffn, int E, int rows, float* y, int32_t* split, hipStream_t s) {
+  constexpr int RB = kRbDown;
+  // cut the reduction (into whole 64-wide chunks, at least 16 per part)
+  // until the grid holds about two waves per SIMD
+  const int nx = (d + 16 * RB * SW - 1) / (16 * RB * SW);
+  int S = 1;
+  while (2 * S <= kMaxDownSplit && nx * E * S * SW < 2048 && ffn / 64 >= 2 * S * 16) S *= 2;
+  dim3 grid(nx, E, S);
+  const size_t c_split = static_cast<size_t>(rows) * d;
+  auto run = [&](auto kern) {
+    kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(h), nullptr, offsets,
+                                  static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, c_split,
+                                  split);
+  };
+  if (token_blocks(rows, E) == 1) run(expert_stream_kernel<false, RB, 1>);
+  else run(expert_stream_kernel<false, RB, 2>);
   return launch_status();
 }
 

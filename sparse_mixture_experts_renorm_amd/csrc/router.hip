@@ -138,20 +138,37 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Each wave takes U consecutive 32-wide slices at a time and issues all
+  // their loads before the first product, so a wave waits for one memory
+  // round trip per U slices (this kernel is latency-bound for small T).
+  // Out-of-range rows, experts and columns load from a valid address and
+  // are replaced by zeros, which keeps the loads unconditional.
+  constexpr int U = 4;
   const int nk = (d + 31) / 32;
-  for (int kc = wave; kc < nk; kc += NW) {
-    const int col = kc * 32 + kq * 8;
-    const bool col_ok = col < d;
-    uint4 a = make_uint4(0, 0, 0, 0);
-    if (row_ok && col_ok) a = *reinterpret_cast<const uint4*>(xrow + col);
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int kc0 = wave * U; kc0 < nk; kc0 += NW * U) {
+    uint4 a[U], b[U][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int e = nb * 16 + r;
-      uint4 b = make_uint4(0, 0, 0, 0);
-      if (e < E && col_ok) b = *reinterpret_cast<const uint4*>(wr + static_cast<size_t>(e) * d + col);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, b), acc[nb], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int col = (kc0 + u) * 32 + kq * 8;
+      const bool col_ok = col < d;
+      const int c = col_ok ? col : 0;
+      a[u] = *reinterpret_cast<const uint4*>(xrow + c);
+      if (!(row_ok && col_ok)) a[u] = zero;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int e = nb * 16 + r;
+        b[u][nb] = *reinterpret_cast<const uint4*>(wr + static_cast<size_t>(min(e, E - 1)) * d + c);
+        if (!(e < E && col_ok)) b[u][nb] = zero;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                          __builtin_bit_cast(bf16x8, b[u][nb]),
+                                                          acc[nb], 0, 0, 0);
   }
   // D layout: lane l holds rows 4*(l/16)+i, column l%16
 #pragma unroll
@@ -232,8 +249,8 @@ moe_status launch_route(const void* x, const void* w_router, const float* bias, 
                                                  E, k, logits, probs, topk_idx, topk_w);
     return launch_status();
   }
-  if (E <= 16) return launch_route_bf16<1, 8>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);
-  if (E <= 32) return launch_route_bf16<2, 8>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);
+  if (E <= 16) return launch_route_bf16<1, 16>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);
+  if (E <= 32) return launch_route_bf16<2, 16>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);
   if (E <= 64) return launch_route_bf16<4, 8>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);
   if (E <= 128) return launch_route_bf16<8, 4>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);
   return launch_route_bf16<16, 4>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);
