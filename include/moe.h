@@ -144,6 +144,28 @@ moe_status moe_forward_profiled(const void* x, const void* w_router, const void*
                                 void* ws, size_t ws_bytes, hipStream_t stream,
                                 hipEvent_t* stage_events);
 
+/* ---- Router statistics --------------------------------------------------
+ * Source: axonml-nn layers/moe.rs (docs.rs), MoELayer::load_balancing_loss
+ * (Switch Transformer form), and MoELayer::expert_utilization for counts.
+ * From the routing probabilities probs [T, E] (fp32, e.g. moe_forward's
+ * probs_out) and the per-expert assignment counts [E] (int32, e.g.
+ * counts_out):
+ *   mean_probs[e] = P_e = (1/T) sum_t probs[t, e]
+ *   frac[e]       = f_e = counts[e] / T        (NULL: not written)
+ *   *lb_loss      = E * sum_e f_e * P_e
+ * f counts all k slots of a token, so sum_e f_e = k and a perfectly even
+ * routing gives lb_loss = k (the page's convention). T = 0 writes zeros
+ * (the page returns 0 before any tokens), so unlike the other entry points
+ * it launches a kernel. Sums run in a fixed order (deterministic).
+ * ws: caller scratch of moe_router_stats_workspace_size(T, E) bytes
+ * (unused when T = 0). Errors: INVALID_ARG for T < 0, E < 1 or a null or
+ * misaligned required pointer; UNSUPPORTED for E > 256;
+ * WORKSPACE_TOO_SMALL. */
+size_t moe_router_stats_workspace_size(int T, int E);
+moe_status moe_router_stats(const float* probs, const int32_t* counts, int T, int E,
+                            float* mean_probs, float* frac, float* lb_loss,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         _p("moe_forward", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp, vp, sz, vp)
         _p("moe_forward_profiled", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp,
            vp, sz, vp, vp)
+        _p("moe_router_stats_workspace_size", sz, i, i)
+        _p("moe_router_stats", i, vp, vp, i, i, vp, vp, vp, vp, sz, vp)
     return _lib
 
 
@@ -165,6 +167,26 @@ def moe_permute(topk_idx, E, stream=None):
     _check(lib().moe_permute(_ptr(topk_idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(st),
                              _ptr(inv), _stream(stream)), "moe_permute")
     return counts, offsets, st, inv
+
+
+def moe_router_stats(probs, counts, stream=None):
+    """Router statistics from probs f32 [T,E] and counts int32 [E]. Returns
+    (mean_probs f32 [E], frac f32 [E], lb_loss f32 [1]) as device tensors."""
+    _dev(probs, counts)
+    assert probs.dtype == torch.float32 and probs.dim() == 2
+    assert counts.dtype == torch.int32 and counts.dim() == 1
+    T, E = probs.shape
+    assert counts.shape[0] == E
+    dev = probs.device
+    mean = torch.empty(E, dtype=torch.float32, device=dev)
+    frac = torch.empty(E, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    n = int(lib().moe_router_stats_workspace_size(T, E))
+    ws = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device=dev)
+    wp, wn = _ws_ptr(ws)
+    _check(lib().moe_router_stats(_ptr(probs), _ptr(counts), T, E, _ptr(mean), _ptr(frac),
+                                  _ptr(loss), wp, wn, _stream(stream)), "moe_router_stats")
+    return mean, frac, loss
 
 
 def _layer_shapes(x, w_gate, w_up, w_down):

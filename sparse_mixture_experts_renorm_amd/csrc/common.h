@@ -99,6 +99,12 @@ moe_status launch_down_stream(const void* h, const int32_t* offsets, const void*
                               int ffn, int E, int rows, float* y, int32_t* split, hipStream_t s);
 // Few rows per expert: the weight-streaming kernels replace the tiled ones.
 inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
+// Router statistics (router_stats.hip): partial sums over router_stats_blocks(T)
+// blocks of `partial` floats per expert.
+int router_stats_blocks(int T);
+moe_status launch_router_stats(const float* probs, const int32_t* counts, int T, int E,
+                               float* mean_probs, float* frac, float* loss, float* partial,
+                               hipStream_t s);
 moe_status launch_combine(const float* y, const int32_t* split, const int32_t* inv_pos,
                           const float* topk_w, int T, int d, int k, void* out, moe_dtype out_dt,
                           hipStream_t s);

@@ -90,6 +90,23 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* co
   return launch_permute(topk_idx, T, E, k, counts, offsets, sorted_token, inv_pos, stream);
 }
 
+size_t moe_router_stats_workspace_size(int T, int E) {
+  if (T < 0 || E < 1 || E > kMaxExperts) return 0;
+  return static_cast<size_t>(router_stats_blocks(T)) * E * sizeof(float);
+}
+
+moe_status moe_router_stats(const float* probs, const int32_t* counts, int T, int E,
+                            float* mean_probs, float* frac, float* lb_loss, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || E < 1) return MOE_INVALID_ARG;
+  if (E > kMaxExperts) return MOE_UNSUPPORTED;
+  if (!ok_ptr(mean_probs) || !ok_ptr(lb_loss) || !ok_opt(frac)) return MOE_INVALID_ARG;
+  if (T > 0 && (!ok_ptr(probs) || !ok_ptr(counts) || !ok_ptr(ws))) return MOE_INVALID_ARG;
+  if (T > 0 && ws_bytes < moe_router_stats_workspace_size(T, E)) return MOE_WORKSPACE_TOO_SMALL;
+  return launch_router_stats(probs, counts, T, E, mean_probs, frac, lb_loss,
+                             static_cast<float*>(ws), stream);
+}
+
 // ev: NULL, or events [2..5] are recorded after the permutation, the gate/up
 // GEMM, the down GEMM and the combine.
 static moe_status run_experts(const void* x, const int32_t* topk_idx, const float* topk_w,

@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(L):
     names = m.declared_symbols()
     assert set(names) == {"moe_status_string", "moe_workspace_size", "moe_route",
                           "moe_route_logits", "moe_permute", "moe_expert_ffn", "moe_forward",
-                          "moe_forward_profiled"}
+                          "moe_forward_profiled", "moe_router_stats_workspace_size",
+                          "moe_router_stats"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -103,6 +104,21 @@ def test_expert_ffn_and_permute_validation(L):
                                   None, p, 1 << 30, None, ev) == INVALID
     assert L.moe_forward_profiled(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, p, F32, None, None,
                                   None, p, 1 << 30, None, None) == INVALID
+
+
+def test_router_stats_validation(L):
+    p = ctypes.c_void_p(256)
+    n = L.moe_router_stats_workspace_size(1000, 8)
+    assert n == 16 * 8 * 4          # 16 blocks of 64 rows, one float per expert each
+    assert L.moe_router_stats_workspace_size(-1, 8) == 0
+    assert L.moe_router_stats_workspace_size(10, 257) == 0
+    assert L.moe_router_stats(p, p, -1, 8, p, None, p, p, n, None) == INVALID
+    assert L.moe_router_stats(p, p, 10, 0, p, None, p, p, n, None) == INVALID
+    assert L.moe_router_stats(p, p, 10, 257, p, None, p, p, n, None) == UNSUPPORTED
+    assert L.moe_router_stats(None, p, 10, 8, p, None, p, p, n, None) == INVALID
+    assert L.moe_router_stats(p, p, 10, 8, None, None, p, p, n, None) == INVALID
+    assert L.moe_router_stats(p, p, 10, 8, p, ctypes.c_void_p(260), p, p, n, None) == INVALID
+    assert L.moe_router_stats(p, p, 1000, 8, p, None, p, p, n - 4, None) == WS_SMALL
 
 
 def test_binding_requires_library(monkeypatch, tmp_path):

@@ -272,6 +272,11 @@ def pin_load_balancing_loss():
     p2, i2, _ = O.route(O.router_logits(x, wr), 2)
     assert O.load_balancing_loss(p2, O.expert_counts(i2, 4)) > 0.0
     assert O.load_balancing_loss(np.zeros((0, 4)), np.zeros(4)) == 0.0
+    # full collapse: every token puts all probability on expert 2 and is
+    # routed there (k = 1): f_2 = P_2 = 1, so the loss is E
+    onehot = np.zeros((T, E))
+    onehot[:, 2] = 1.0
+    assert O.load_balancing_loss(onehot, np.eye(E)[2] * T) == E
 
 
 def pin_bf16_widening():
