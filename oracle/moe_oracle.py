@@ -47,7 +47,19 @@ design notes of the repository):
     reach the 1.45B the Mixtral page states).
   * The combine weight of expert S_j for token t is w_j alone (axonml and
     Mixtral pages), not the sum of the token's gates (skills page's MoELayer).
-  * No capacity limit: every token reaches its k experts.
+  * No capacity limit by default: every token reaches its k experts. With a
+    capacity factor cf > 0 (KempnerForge ``ModelConfig.moe_capacity_factor``:
+    0 means no dropping, a positive value caps the tokens per expert) each
+    expert keeps at most C = ceil(cf * T * k / E) assignments, the first C
+    in token order; a dropped assignment adds nothing and the token's other
+    weights are left as routed (not renormalised again).
+  * RMSNorm before the layer follows the Mixtral page's ``nn.RMSNorm``:
+    x / sqrt(mean(x^2) + eps) * weight (eps inside the root; the skills
+    page's variant adds eps to the root instead and is not followed); the
+    block adds the un-normalised input back (``moe_residual``).
+  * Shared experts (KempnerForge ``moe_shared_experts``: experts that process
+    all tokens) are SwiGLU FFNs applied to every token and added with
+    weight 1.
   * Inputs must be finite (axonml's sort panics on NaN); asserted here.
 """
 from __future__ import annotations
@@ -57,7 +69,8 @@ import numpy as np
 __all__ = [
     "widen", "router_logits", "softmax", "select_top_k", "renormalise", "route",
     "expert_counts", "permute", "swiglu_expert", "combine", "expert_ffn",
-    "moe_forward", "dense_bruteforce", "load_balancing_loss",
+    "moe_forward", "dense_bruteforce", "load_balancing_loss", "capacity", "rms_norm",
+    "shared_experts",
 ]
 
 
@@ -139,30 +152,46 @@ def expert_counts(idx, E: int) -> np.ndarray:
     return np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.int64)[:E]
 
 
-def permute(idx, E: int):
+def capacity(T: int, E: int, k: int, capacity_factor: float):
+    """Assignments each expert may keep: None (no limit) for a factor of 0,
+    else ceil(cf * T * k / E) (KempnerForge ``moe_capacity_factor``, read as
+    a multiple of the even share T * k / E)."""
+    if capacity_factor < 0:
+        raise ValueError("capacity_factor must be >= 0")
+    if capacity_factor == 0:
+        return None
+    return int(np.ceil(capacity_factor * T * k / E))
+
+
+def permute(idx, E: int, cap=None):
     """Per-expert token lists, as axonml ``MoELayer::forward`` builds them:
     experts in ascending order, and within an expert the tokens that chose it
-    in ascending token order.
+    in ascending token order. With ``cap`` only the first ``cap`` tokens of
+    each expert are kept.
 
-    Returns counts [E], offsets [E+1] (offsets[e] = start of expert e's rows),
-    sorted_token [T*k] (token of each row), inv_pos [T*k] (row of assignment
-    t*k + j)."""
+    Returns counts [E] (rows kept per expert), offsets [E+1] (offsets[e] =
+    start of expert e's rows), sorted_token [rows] (token of each row) and
+    inv_pos [T*k] (row of assignment t*k + j, -1 if it was dropped)."""
     idx = np.asarray(idx)
     T, k = idx.shape
-    counts = expert_counts(idx, E)
+    counts = np.zeros(E, np.int64)
     offsets = np.zeros(E + 1, np.int64)
-    sorted_token = np.empty(T * k, np.int64)
-    inv_pos = np.empty(T * k, np.int64)
+    inv_pos = np.full(T * k, -1, np.int64)
+    lists = []
     row = 0
     for e in range(E):
         offsets[e] = row
         tok, slot = np.nonzero(idx == e)  # row-major: ascending token
+        if cap is not None:
+            tok, slot = tok[:cap], slot[:cap]
         n = tok.size
-        sorted_token[row:row + n] = tok
+        counts[e] = n
+        lists.append(tok)
         inv_pos[tok * k + slot] = np.arange(row, row + n)
         row += n
     offsets[E] = row
-    return counts, offsets, sorted_token, inv_pos
+    sorted_token = np.concatenate(lists) if lists else np.zeros(0, np.int64)
+    return counts, offsets, sorted_token.astype(np.int64), inv_pos
 
 
 # ----------------------------------------------------------------- experts --
@@ -195,9 +224,11 @@ def combine(T: int, d: int, idx, w, expert_rows) -> np.ndarray:
     return out
 
 
-def expert_ffn(x, idx, w, w_gate, w_up, w_down, E: int | None = None) -> np.ndarray:
+def expert_ffn(x, idx, w, w_gate, w_up, w_down, E: int | None = None, cap=None) -> np.ndarray:
     """Rows 5-7 of the layer for a given routing (idx, w): gather each expert's
-    tokens, run its SwiGLU FFN, combine. Experts with no token are skipped."""
+    tokens (the first ``cap`` of them if a capacity is set), run its SwiGLU
+    FFN, combine. Experts with no token are skipped; a token an expert did
+    not keep gets nothing from it."""
     idx = np.asarray(idx)
     xw = widen(x)
     T, d = xw.shape
@@ -205,23 +236,62 @@ def expert_ffn(x, idx, w, w_gate, w_up, w_down, E: int | None = None) -> np.ndar
     rows = {}
     for e in range(E):
         tok = np.nonzero((idx == e).any(axis=-1))[0]
+        if cap is not None:
+            tok = tok[:cap]
         if tok.size == 0:
             continue
         rows[e] = (tok, swiglu_expert(xw[tok], w_gate[e], w_up[e], w_down[e]))
     return combine(T, d, idx, w, rows)
 
 
-def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, bias=None):
+def rms_norm(x, weight, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * weight over the last axis (the Mixtral
+    page's ``nn.RMSNorm`` before the MoE layer)."""
+    xw = widen(x)
+    r = np.sqrt(np.mean(xw * xw, axis=-1, keepdims=True) + eps)
+    return xw / r * widen(weight)
+
+
+def shared_experts(x, s_gate, s_up, s_down) -> np.ndarray:
+    """Sum over the shared experts of their SwiGLU FFN on every token
+    (KempnerForge ``moe_shared_experts``); weights [S, ffn_s, d] and
+    [S, d, ffn_s]."""
+    xw = widen(x)
+    out = np.zeros_like(xw)
+    for i in range(np.asarray(s_gate).shape[0]):
+        out += swiglu_expert(xw, s_gate[i], s_up[i], s_down[i])
+    return out
+
+
+def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, bias=None, capacity_factor=0.0,
+                norm_weight=None, norm_eps=1e-5, residual=False, shared=None):
     """The whole layer on x [T, d]: router logits, route, counts, per-expert
     SwiGLU, weighted combine (axonml ``MoELayer::forward``).
 
-    Returns (out [T,d], dict(logits, probs, idx, w, counts))."""
-    L = router_logits(x, w_router, bias)
+    Options (all off by default): ``capacity_factor`` (see ``capacity``);
+    ``norm_weight``: the layer runs on rms_norm(x, norm_weight, norm_eps);
+    ``residual``: x (not normalised) is added to the output (the Mixtral
+    block's ``moe_residual``); ``shared`` = (s_gate, s_up, s_down): shared
+    experts added to every token.
+
+    Returns (out [T,d], dict(logits, probs, idx, w, counts, routed_counts)),
+    counts being the rows each expert kept."""
+    xin = widen(x)
+    xl = xin if norm_weight is None else rms_norm(xin, norm_weight, norm_eps)
+    L = router_logits(xl, w_router, bias)
     probs, idx, w = route(L, k)
     E = np.asarray(w_router).shape[0]
-    out = expert_ffn(x, idx, w, w_gate, w_up, w_down, E)
-    return out, {"logits": L, "probs": probs, "idx": idx, "w": w,
-                 "counts": expert_counts(idx, E)}
+    T = xin.shape[0]
+    cap = capacity(T, E, k, capacity_factor)
+    out = expert_ffn(xl, idx, w, w_gate, w_up, w_down, E, cap)
+    if shared is not None:
+        out = out + shared_experts(xl, *shared)
+    if residual:
+        out = out + xin
+    routed = expert_counts(idx, E)
+    kept = routed if cap is None else np.minimum(routed, cap)
+    return out, {"logits": L, "probs": probs, "idx": idx, "w": w, "counts": kept,
+                 "routed_counts": routed}
 
 
 def dense_bruteforce(x, w_router, w_gate, w_up, w_down, k: int, bias=None) -> np.ndarray:

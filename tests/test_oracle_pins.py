@@ -288,6 +288,96 @@ def pin_bf16_widening():
     assert np.signbit(got[3])
 
 
+def pin_capacity_bruteforce():
+    """Each expert keeps the first C tokens (ascending) that chose it, found
+    by walking the tokens with a counter per expert; the kept rows are laid
+    out expert by expert. C = ceil(cf * T * k / E); a factor of 0 means no
+    limit (KempnerForge: 0 = no drop)."""
+    T, E, k = 50, 5, 2
+    idx, _ = wl.make_routing(T, E, k, "one_heavy", seed=2)
+    assert O.capacity(T, E, k, 0.0) is None
+    assert O.capacity(T, E, k, 1.0) == 20 and O.capacity(T, E, k, 0.26) == 6
+    for cf in (0.26, 0.5, 1.0, 1.25):
+        cap = O.capacity(T, E, k, cf)
+        counts, offsets, st, inv = O.permute(idx, E, cap)
+        seen = [0] * E
+        want_rows = [[] for _ in range(E)]
+        kept = np.zeros((T, k), bool)
+        for t in range(T):
+            for j in range(k):
+                e = int(idx[t, j])
+                if seen[e] < cap:
+                    kept[t, j] = True
+                    want_rows[e].append(t)
+                seen[e] += 1
+        assert [len(r) for r in want_rows] == list(counts)
+        assert list(st) == [t for r in want_rows for t in r]
+        assert offsets[-1] == kept.sum() == len(st)
+        for t in range(T):
+            for j in range(k):
+                p = inv[t * k + j]
+                if kept[t, j]:
+                    assert st[p] == t and offsets[idx[t, j]] <= p < offsets[idx[t, j] + 1]
+                else:
+                    assert p == -1
+    # a cap at or above every count changes nothing
+    big = O.capacity(T, E, k, 10.0)
+    for a, b in zip(O.permute(idx, E, big), O.permute(idx, E)):
+        assert np.array_equal(a, b)
+
+
+def pin_capacity_constant_input():
+    """Identical tokens all choose the same k experts, so with capacity C
+    exactly the first C tokens keep their outputs and the rest get zero."""
+    T, d, ffn, E, k = 24, 32, 16, 4, 2
+    x = np.full((T, d), 0.1)
+    _, wr, wg, wu, wd = _layer(T, d, ffn, E, seed=21)
+    full, _ = O.moe_forward(x, wr, wg, wu, wd, k)
+    cf = 0.5                      # C = ceil(0.5 * 24 * 2 / 4) = 6
+    out, aux = O.moe_forward(x, wr, wg, wu, wd, k, capacity_factor=cf)
+    assert O.capacity(T, E, k, cf) == 6
+    assert np.array_equal(out[:6], full[:6]) and not out[6:].any()
+    assert sorted(aux["counts"][aux["counts"] > 0]) == [6, 6]
+    assert sorted(aux["routed_counts"][aux["routed_counts"] > 0]) == [T, T]
+
+
+def pin_rms_norm_library():
+    """The norm equals torch's rms_norm (float64, CPU), is invariant to
+    scaling the input when eps = 0, and maps a constant row c to
+    c / sqrt(c^2 + eps) times the weight."""
+    x = _rand((7, 48), 31) * 3.0
+    g = _rand((48,), 32)
+    for eps in (1e-5, 1e-2, 0.0):
+        want = torch.nn.functional.rms_norm(torch.from_numpy(x), (48,), torch.from_numpy(g),
+                                            eps).numpy()
+        np.testing.assert_allclose(O.rms_norm(x, g, eps), want, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O.rms_norm(8.0 * x, g, 0.0), O.rms_norm(x, g, 0.0), rtol=1e-14)
+    c = np.full((1, 16), 0.5)
+    np.testing.assert_allclose(O.rms_norm(c, np.ones(16), 0.04), np.full((1, 16), 0.5 / 0.53851648071345),
+                               rtol=1e-12)
+
+
+def pin_residual_and_shared():
+    """With W_down = 0 the block returns its input exactly; shared experts
+    add torch's SwiGLU of the normalised input; the residual is the
+    un-normalised input."""
+    T, d, ffn, E, k = 20, 32, 24, 4, 2
+    x, wr, wg, wu, wd = _layer(T, d, ffn, E, seed=41)
+    g = 1.0 + _rand((d,), 42, 0.1)
+    out, _ = O.moe_forward(x, wr, wg, wu, np.zeros_like(wd), k, norm_weight=g, norm_eps=1e-5,
+                           residual=True)
+    assert np.array_equal(out, x)
+    rng = np.random.default_rng(43)
+    sg, su = rng.standard_normal((2, 12, d)) * 0.02, rng.standard_normal((2, 12, d)) * 0.02
+    sd = rng.standard_normal((2, d, 12)) * 0.02
+    base, _ = O.moe_forward(x, wr, wg, wu, wd, k, norm_weight=g, norm_eps=1e-5)
+    withs, _ = O.moe_forward(x, wr, wg, wu, wd, k, norm_weight=g, norm_eps=1e-5, residual=True,
+                             shared=(sg, su, sd))
+    xn = torch.nn.functional.rms_norm(torch.from_numpy(x), (d,), torch.from_numpy(g), 1e-5).numpy()
+    want = base + x + _torch_ffn(xn, sg[0], su[0], sd[0]) + _torch_ffn(xn, sg[1], su[1], sd[1])
+    np.testing.assert_allclose(withs, want, rtol=1e-12, atol=1e-14)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -413,7 +503,51 @@ def _m_offsets_inclusive(idx, E):
 
 _REAL = {"permute": O.permute}
 
+_orig_capacity, _orig_permute, _orig_rms, _orig_shared, _orig_ffn = (
+    O.capacity, O.permute, O.rms_norm, O.shared_experts, O.expert_ffn)
+
+
+def _m_capacity_floor(T, E, k, cf):
+    return None if cf == 0 else int(np.floor(cf * T * k / E))
+
+
+def _m_capacity_plus_one(T, E, k, cf):
+    c = _orig_capacity(T, E, k, cf)
+    return None if c is None else c + 1
+
+
+def _m_permute_keeps_last(idx, E, cap=None):
+    if cap is None:
+        return _orig_permute(idx, E)
+    # keep the last cap tokens of each expert instead of the first
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    rev = idx[::-1]
+    counts, offsets, st, inv = _orig_permute(rev, E, cap)
+    st = (T - 1 - st)
+    return counts, offsets, st, inv
+
+
+def _m_rms_eps_outside(x, weight, eps):
+    xw = O.widen(x)
+    return xw / (np.sqrt(np.mean(xw * xw, axis=-1, keepdims=True)) + eps) * O.widen(weight)
+
+
+def _m_shared_half(x, a, b, c):
+    return 0.5 * _orig_shared(x, a, b, c)
+
+
+def _m_ffn_ignores_cap(x, idx, w, wg, wu, wd, E=None, cap=None):
+    return _orig_ffn(x, idx, w, wg, wu, wd, E)
+
+
 MUTANTS = {
+    "capacity_floor": ("capacity", _m_capacity_floor),
+    "capacity_plus_one": ("capacity", _m_capacity_plus_one),
+    "permute_keeps_last": ("permute", _m_permute_keeps_last),
+    "rms_eps_outside_root": ("rms_norm", _m_rms_eps_outside),
+    "shared_half_weight": ("shared_experts", _m_shared_half),
+    "ffn_ignores_capacity": ("expert_ffn", _m_ffn_ignores_cap),
     "no_renormalisation": ("renormalise", _m_no_renorm),
     "gate_sum_combine": ("combine", _m_gate_sum_combine),
     "silu_on_up": ("swiglu_expert", _m_silu_on_up),
