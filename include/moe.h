@@ -166,6 +166,57 @@ moe_status moe_router_stats(const float* probs, const int32_t* counts, int T, in
                             float* mean_probs, float* frac, float* lb_loss,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Extended forward: the layer inside a Mixtral-style block ------------
+ * Same layer as moe_forward, with options (all off when zeroed):
+ *   capacity_factor  KempnerForge ModelConfig.moe_capacity_factor (0 = no
+ *                    dropping). With cf > 0 each expert keeps at most
+ *                    C = ceil(cf * T * k / E) assignments, the first C in
+ *                    token order; a dropped assignment contributes nothing
+ *                    and the token's other weights stay as routed.
+ *   norm_weight      [d] in dt, or NULL. When set, the layer (router and
+ *                    experts) runs on RMSNorm(x) = x / sqrt(mean(x^2) +
+ *                    norm_eps) * norm_weight, the post-attention nn.RMSNorm
+ *                    of the Mixtral block page; the normalised input is
+ *                    stored in dt (bf16: rounded to nearest even). norm_eps
+ *                    must be > 0.
+ *   residual         nonzero: out = x + layer(...), with the un-normalised x
+ *                    (the Mixtral block's moe_residual add), added in fp32.
+ *   n_shared, shared_ffn, shared_gate [n_shared, shared_ffn, d],
+ *   shared_up [n_shared, shared_ffn, d], shared_down [n_shared, d,
+ *                    shared_ffn] (dt): KempnerForge moe_shared_experts,
+ *                    SwiGLU experts every token passes through, added with
+ *                    weight 1 after the routed experts.
+ * Outputs as moe_forward; counts_out are the rows each expert kept and
+ * routed_counts_out (nullable) the assignments before the capacity cut (the
+ * counts the load-balancing loss uses).
+ * Workspace: moe_forward_ext_workspace_size(...) bytes, 256-byte aligned.
+ * Errors as moe_forward, plus INVALID_ARG for opt == NULL, a negative or
+ * non-finite capacity factor, norm_eps <= 0, n_shared < 0, shared_ffn < 1
+ * or a null or misaligned shared weight; UNSUPPORTED for n_shared > 16 or
+ * shared_ffn % 16 != 0. */
+typedef struct {
+  float capacity_factor;
+  const void* norm_weight;
+  float norm_eps;
+  int residual;
+  int n_shared;
+  int shared_ffn;
+  const void* shared_gate;
+  const void* shared_up;
+  const void* shared_down;
+} moe_options;
+
+size_t moe_forward_ext_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt,
+                                      const moe_options* opt);
+moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_gate,
+                           const void* w_up, const void* w_down, const float* router_bias,
+                           int T, int d, int ffn, int E, int k, moe_dtype dt,
+                           const moe_options* opt,
+                           void* out, moe_dtype out_dt,
+                           float* logits_out, float* probs_out, int32_t* counts_out,
+                           int32_t* routed_counts_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

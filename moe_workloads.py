@@ -43,6 +43,7 @@ WEIGHT_STD = 0.02
 
 TID_X, TID_ROUTER, TID_GATE, TID_UP, TID_DOWN = 0, 1, 2, 3, 4
 TID_LOGITS, TID_ROUTING_IDX, TID_ROUTING_W = 16, 17, 18
+TID_NORM, TID_SHARED_GATE, TID_SHARED_UP, TID_SHARED_DOWN = 5, 6, 7, 8
 
 
 def ffn_hidden_dim(dim: int, ffn_dim_multiplier: float = 1.0) -> int:
@@ -190,6 +191,19 @@ def make_custom_inputs(T: int, d: int, ffn: int, E: int, dtype: str, seed: int =
                        bias: bool = False) -> dict:
     """Same recipe as :func:`make_layer_inputs` for an arbitrary shape."""
     return make_layer_inputs(Workload("custom", T, d, ffn, E, 1, dtype, bias), seed)
+
+
+def make_block_extras(d: int, n_shared: int, shared_ffn: int, dtype: str, seed: int = 0) -> dict:
+    """Inputs of the block options: an RMSNorm weight [d] drawn around 1
+    (1 + 0.1 N(0,1)) and n_shared shared experts' weights (0.02 N(0,1)):
+    s_gate, s_up [n_shared, shared_ffn, d], s_down [n_shared, d, shared_ffn]."""
+    g = 1.0 + normal_f32(seed, TID_NORM, d, 0.1)
+    out = {"norm_weight": f32_to_bf16_bits(g) if dtype == "bf16" else g.astype(np.float32)}
+    if n_shared > 0:
+        out["s_gate"] = _tensor(seed, TID_SHARED_GATE, (n_shared, shared_ffn, d), WEIGHT_STD, dtype)
+        out["s_up"] = _tensor(seed, TID_SHARED_UP, (n_shared, shared_ffn, d), WEIGHT_STD, dtype)
+        out["s_down"] = _tensor(seed, TID_SHARED_DOWN, (n_shared, d, shared_ffn), WEIGHT_STD, dtype)
+    return out
 
 
 # --------------------------------------------------------------------------

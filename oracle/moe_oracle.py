@@ -57,6 +57,9 @@ design notes of the repository):
     x / sqrt(mean(x^2) + eps) * weight (eps inside the root; the skills
     page's variant adds eps to the root instead and is not followed); the
     block adds the un-normalised input back (``moe_residual``).
+  * When the layer's inputs are bf16, the normalised input is a bf16 tensor
+    too (it is the input of a bf16 layer): the exact RMSNorm value is
+    rounded once to the nearest bf16, ties to even (``round_to_bf16``).
   * Shared experts (KempnerForge ``moe_shared_experts``: experts that process
     all tokens) are SwiGLU FFNs applied to every token and added with
     weight 1.
@@ -70,7 +73,7 @@ __all__ = [
     "widen", "router_logits", "softmax", "select_top_k", "renormalise", "route",
     "expert_counts", "permute", "swiglu_expert", "combine", "expert_ffn",
     "moe_forward", "dense_bruteforce", "load_balancing_loss", "capacity", "rms_norm",
-    "shared_experts",
+    "shared_experts", "round_to_bf16",
 ]
 
 
@@ -252,6 +255,15 @@ def rms_norm(x, weight, eps: float) -> np.ndarray:
     return xw / r * widen(weight)
 
 
+def round_to_bf16(a) -> np.ndarray:
+    """Nearest bfloat16 value of each element (8 significant bits, ties to
+    even), as float64. Normal range only (the values rounded here are
+    normalised activations)."""
+    a = np.asarray(a, np.float64)
+    m, e = np.frexp(a)                 # a = m * 2^e with 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)   # np.round: half to even
+
+
 def shared_experts(x, s_gate, s_up, s_down) -> np.ndarray:
     """Sum over the shared experts of their SwiGLU FFN on every token
     (KempnerForge ``moe_shared_experts``); weights [S, ffn_s, d] and
@@ -278,6 +290,8 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, bias=None, capacity_f
     counts being the rows each expert kept."""
     xin = widen(x)
     xl = xin if norm_weight is None else rms_norm(xin, norm_weight, norm_eps)
+    if norm_weight is not None and np.asarray(x).dtype == np.uint16:
+        xl = round_to_bf16(xl)  # a bf16 layer's normalised input is bf16
     L = router_logits(xl, w_router, bias)
     probs, idx, w = route(L, k)
     E = np.asarray(w_router).shape[0]

@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
            vp, sz, vp, vp)
         _p("moe_router_stats_workspace_size", sz, i, i)
         _p("moe_router_stats", i, vp, vp, i, i, vp, vp, vp, vp, sz, vp)
+        _p("moe_forward_ext_workspace_size", sz, i, i, i, i, i, i, vp)
+        _p("moe_forward_ext", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, vp, vp, vp,
+           vp, vp, sz, vp)
     return _lib
 
 
@@ -259,4 +262,80 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, k, router_bias=None, out_dtyp
         assert len(stage_events) == 6
         arr = (ctypes.c_void_p * 6)(*[e.cuda_event for e in stage_events])
         _check(lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
+    return (out, extras) if extras else out
+
+
+class MoeOptions(ctypes.Structure):
+    """Mirror of the C struct moe_options (include/moe.h)."""
+    _fields_ = [("capacity_factor", ctypes.c_float), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float), ("residual", ctypes.c_int),
+                ("n_shared", ctypes.c_int), ("shared_ffn", ctypes.c_int),
+                ("shared_gate", ctypes.c_void_p), ("shared_up", ctypes.c_void_p),
+                ("shared_down", ctypes.c_void_p)]
+
+
+def _options(capacity_factor, norm_weight, norm_eps, residual, shared):
+    o = MoeOptions()
+    o.capacity_factor = float(capacity_factor)
+    o.norm_weight = None if norm_weight is None else norm_weight.data_ptr()
+    o.norm_eps = float(norm_eps)
+    o.residual = 1 if residual else 0
+    if shared is not None:
+        sg, su, sd = shared
+        o.n_shared, o.shared_ffn = sg.shape[0], sg.shape[1]
+        o.shared_gate, o.shared_up, o.shared_down = sg.data_ptr(), su.data_ptr(), sd.data_ptr()
+    return o
+
+
+def moe_forward_ext_workspace_size(T, d, ffn, E, k, dtype, capacity_factor=0.0, norm_weight=None,
+                                   norm_eps=1e-5, residual=False, shared=None) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    o = _options(capacity_factor, norm_weight, norm_eps, residual, shared)
+    return int(lib().moe_forward_ext_workspace_size(T, d, ffn, E, k, dt, ctypes.byref(o)))
+
+
+def moe_forward_ext(x, w_router, w_gate, w_up, w_down, k, router_bias=None, capacity_factor=0.0,
+                    norm_weight=None, norm_eps=1e-5, residual=False, shared=None,
+                    out_dtype=torch.float32, out=None, ws=None, want_logits=False,
+                    want_probs=False, want_counts=False, want_routed_counts=False, stream=None):
+    """The layer with the block options of moe_forward_ext: capacity factor,
+    RMSNorm of the input (norm_weight [d]), residual add, shared experts
+    (shared = (s_gate [S,ffn_s,d], s_up [S,ffn_s,d], s_down [S,d,ffn_s])).
+    Returns out [T, d], or (out, extras) when any want_* flag is set."""
+    _dev(x, w_router, w_gate, w_up, w_down, router_bias, norm_weight, out, ws)
+    T, d, ffn, E = _layer_shapes(x, w_gate, w_up, w_down)
+    assert w_router.shape == (E, d) and w_router.dtype == x.dtype
+    if norm_weight is not None:
+        assert norm_weight.shape == (d,) and norm_weight.dtype == x.dtype
+    if shared is not None:
+        _dev(*shared)
+        sg, su, sd = shared
+        S, sffn, d2 = sg.shape
+        assert d2 == d and su.shape == (S, sffn, d) and sd.shape == (S, d, sffn)
+        assert sg.dtype == su.dtype == sd.dtype == x.dtype
+    dev = x.device
+    o = _options(capacity_factor, norm_weight, norm_eps, residual, shared)
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=dev)
+    if ws is None:
+        n = int(lib().moe_forward_ext_workspace_size(T, d, ffn, E, k, _dt(x), ctypes.byref(o)))
+        if n == 0:
+            raise ValueError("invalid or unsupported shape or options")
+        ws = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+    extras = {}
+    if want_logits:
+        extras["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if want_probs:
+        extras["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if want_counts:
+        extras["counts"] = torch.empty(E, dtype=torch.int32, device=dev)
+    if want_routed_counts:
+        extras["routed_counts"] = torch.empty(E, dtype=torch.int32, device=dev)
+    wp, wn = _ws_ptr(ws)
+    _check(lib().moe_forward_ext(_ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                 _ptr(router_bias), T, d, ffn, E, k, _dt(x), ctypes.byref(o),
+                                 _ptr(out), _dt(out), _ptr(extras.get("logits")),
+                                 _ptr(extras.get("probs")), _ptr(extras.get("counts")),
+                                 _ptr(extras.get("routed_counts")), wp, wn, _stream(stream)),
+           "moe_forward_ext")
     return (out, extras) if extras else out

@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["router.hip", "router_stats.hip", "permute.hip", "expert_gemm.hip", "expert_stream.hip",
-           "combine.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "router_stats.hip", "permute.hip", "norm.hip", "expert_gemm.hip",
+           "expert_stream.hip", "combine.hip", "moe_api.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

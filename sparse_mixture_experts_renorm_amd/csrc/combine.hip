@@ -12,6 +12,12 @@
 // the sum of its S parts in part order, then weighted. Each thread owns 8
 // consecutive columns of one token (two 16-byte loads per term); a
 // workgroup covers 2048 columns.
+//
+// Block options (the extended forward): after the k routed terms come the
+// outputs of the shared experts, each with weight 1 and in expert order
+// (KempnerForge moe_shared_experts), and then the residual input (the
+// Mixtral block's moe_residual add), all in fp32 before the one rounding to
+// the output dtype.
 #include "common.h"
 
 namespace moe {
@@ -26,6 +32,17 @@ __device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
 }
 
 template <typename OT>
@@ -43,13 +60,22 @@ __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float v[8]) {
                                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
 
-template <typename YT, typename OT>
-__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
+struct CombineExtra {
+  const float* ys;          // shared experts' outputs: parts of [n_shared * T, d], or null
+  const int32_t* ys_split;  // number of parts in ys
+  size_t ys_stride;         // elements between parts
+  int n_shared, T;
+  const void* resid;        // residual input [T, d] (fp32 or bf16), or null
+};
+
+// RES: 0 no residual, 1 fp32 residual, 2 bf16 residual; SH: shared experts.
+template <typename OT, int RES, bool SH>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ split,
                                                       size_t split_stride,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int d, int k,
-                                                      OT* __restrict__ out) {
+                                                      CombineExtra ex, OT* __restrict__ out) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (col >= d) return;
@@ -59,35 +85,93 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
     const int p = inv_pos[static_cast<size_t>(t) * k + j];
     if (p < 0) continue;
     const float wj = w[static_cast<size_t>(t) * k + j];
-    const YT* yp = y + static_cast<size_t>(p) * d + col;
+    const float* yp = y + static_cast<size_t>(p) * d + col;
     float v[8];
-    load8<YT>(yp, v);
+    load8<float>(yp, v);
     for (int s = 1; s < S; ++s) {
       float u[8];
-      load8<YT>(yp + s * split_stride, u);
+      load8<float>(yp + s * split_stride, u);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] += u[i];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
   }
+  if constexpr (SH) {
+    const int Ss = *ex.ys_split;
+    for (int sh = 0; sh < ex.n_shared; ++sh) {
+      const float* yp = ex.ys + (static_cast<size_t>(sh) * ex.T + t) * d + col;
+      float v[8];
+      load8<float>(yp, v);
+      for (int s = 1; s < Ss; ++s) {
+        float u[8];
+        load8<float>(yp + s * ex.ys_stride, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += u[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  }
+  if constexpr (RES != 0) {
+    float r[8];
+    if constexpr (RES == 1)
+      load8<float>(static_cast<const float*>(ex.resid) + static_cast<size_t>(t) * d + col, r);
+    else
+      load8<bf16_t>(static_cast<const bf16_t*>(ex.resid) + static_cast<size_t>(t) * d + col, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += r[i];
+  }
   store8<OT>(out + static_cast<size_t>(t) * d + col, acc);
+}
+
+template <typename OT, int RES, bool SH>
+void combine_launch(dim3 grid, hipStream_t s, const float* y, const int32_t* split, size_t stride,
+                    const int32_t* inv_pos, const float* w, int d, int k, const CombineExtra& ex,
+                    void* out) {
+  combine_kernel<OT, RES, SH><<<grid, 256, 0, s>>>(y, split, stride, inv_pos, w, d, k, ex,
+                                                   static_cast<OT*>(out));
+}
+
+template <typename OT>
+void combine_dispatch(dim3 grid, hipStream_t s, const float* y, const int32_t* split,
+                      size_t stride, const int32_t* inv_pos, const float* w, int d, int k,
+                      const CombineExtra& ex, int res, void* out) {
+  const bool sh = ex.n_shared > 0;
+  if (res == 0) {
+    if (sh) combine_launch<OT, 0, true>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    else combine_launch<OT, 0, false>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+  } else if (res == 1) {
+    if (sh) combine_launch<OT, 1, true>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    else combine_launch<OT, 1, false>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+  } else {
+    if (sh) combine_launch<OT, 2, true>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    else combine_launch<OT, 2, false>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+  }
 }
 
 }  // namespace
 
+moe_status launch_combine_ext(const float* y, const int32_t* split, const int32_t* inv_pos,
+                              const float* topk_w, int T, int d, int k, const float* ys,
+                              const int32_t* ys_split, int n_shared, const void* resid,
+                              moe_dtype resid_dt, void* out, moe_dtype out_dt, hipStream_t s) {
+  dim3 grid(T, (d + 2047) / 2048);
+  const size_t stride = static_cast<size_t>(T) * k * d;
+  CombineExtra ex{ys, ys_split, static_cast<size_t>(T) * n_shared * d, n_shared, T, resid};
+  const int res = resid == nullptr ? 0 : (resid_dt == MOE_F32 ? 1 : 2);
+  if (out_dt == MOE_F32)
+    combine_dispatch<float>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
+  else
+    combine_dispatch<bf16_t>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
+  return launch_status();
+}
+
 moe_status launch_combine(const float* y, const int32_t* split, const int32_t* inv_pos,
                           const float* topk_w, int T, int d, int k, void* out, moe_dtype out_dt,
                           hipStream_t s) {
-  dim3 grid(T, (d + 2047) / 2048);
-  const size_t stride = static_cast<size_t>(T) * k * d;
-  if (out_dt == MOE_F32)
-    combine_kernel<float, float><<<grid, 256, 0, s>>>(y, split, stride, inv_pos, topk_w, d, k,
-                                                      static_cast<float*>(out));
-  else
-    combine_kernel<float, bf16_t><<<grid, 256, 0, s>>>(y, split, stride, inv_pos, topk_w, d, k,
-                                                       static_cast<bf16_t*>(out));
-  return launch_status();
+  return launch_combine_ext(y, split, inv_pos, topk_w, T, d, k, nullptr, nullptr, 0, nullptr,
+                            MOE_F32, out, out_dt, s);
 }
 
 }  // namespace moe

@@ -77,15 +77,56 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   return w;
 }
 
+// Extra regions of the extended forward's workspace, after the base layout.
+struct ExtWorkspace {
+  Workspace base;
+  void* xn;               // [T, d] in dt: the normalised input (RMSNorm on)
+  int32_t* st_s;          // [n_shared*T] shared experts' rows (identity)
+  int32_t* off_s;         // [n_shared+1]
+  void* h_s;              // [n_shared*T, shared_ffn] in dt
+  float* y_s;             // [kMaxDownSplit, n_shared*T, d] fp32
+  int32_t* split_s;       // [1]
+  size_t bytes;
+};
+
+inline ExtWorkspace carve_ext_workspace(void* base, int T, int d, int ffn, int E, int k,
+                                        moe_dtype dt, bool norm, int n_shared, int shared_ffn) {
+  ExtWorkspace w{};
+  w.base = carve_workspace(base, T, d, ffn, E, k, dt);
+  const size_t es = dt == MOE_BF16 ? 2 : 4;
+  const size_t ts = static_cast<size_t>(T) * n_shared;
+  char* p = static_cast<char*>(base);
+  size_t off = w.base.bytes;
+  auto take = [&](size_t n) { char* r = p ? p + off : nullptr; off += align256(n); return r; };
+  if (norm) w.xn = take(static_cast<size_t>(T) * d * es);
+  if (n_shared > 0) {
+    w.st_s = reinterpret_cast<int32_t*>(take(ts * 4));
+    w.off_s = reinterpret_cast<int32_t*>(take(static_cast<size_t>(n_shared + 1) * 4));
+    w.h_s = take(ts * static_cast<size_t>(shared_ffn) * es);
+    w.y_s = reinterpret_cast<float*>(take(kMaxDownSplit * ts * static_cast<size_t>(d) * 4));
+    w.split_s = reinterpret_cast<int32_t*>(take(4));
+  }
+  w.bytes = off;
+  return w;
+}
+
+constexpr int kMaxShared = 16;  // library limit on shared experts
+
 // ---- launchers (defined in the kernel files) ----
 moe_status launch_route(const void* x, const void* w_router, const float* bias, int T, int d,
                         int E, int k, moe_dtype dt, float* logits, float* probs,
                         int32_t* topk_idx, float* topk_w, hipStream_t s);
 moe_status launch_route_logits(const float* logits, int T, int E, int k, float* probs,
                                int32_t* topk_idx, float* topk_w, hipStream_t s);
-moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
-                          hipStream_t s);
+// cap: most rows an expert keeps (>= T: no limit); routed_counts may be null.
+moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int cap, int32_t* counts,
+                          int32_t* routed_counts, int32_t* offsets, int32_t* sorted_token,
+                          int32_t* inv_pos, hipStream_t s);
+// S shared experts over all T tokens: rows s*T + t hold token t.
+moe_status launch_identity_rows(int T, int S, int32_t* sorted_token, int32_t* offsets,
+                                hipStream_t s);
+moe_status launch_rms_norm(const void* x, const void* g, int T, int d, float eps, moe_dtype dt,
+                           void* xn, hipStream_t s);
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
                           int k, moe_dtype dt, void* h, hipStream_t s);
@@ -108,5 +149,11 @@ moe_status launch_router_stats(const float* probs, const int32_t* counts, int T,
 moe_status launch_combine(const float* y, const int32_t* split, const int32_t* inv_pos,
                           const float* topk_w, int T, int d, int k, void* out, moe_dtype out_dt,
                           hipStream_t s);
+// ys: outputs of n_shared shared experts (their own split count ys_split);
+// resid: [T, d] in resid_dt added last; both optional.
+moe_status launch_combine_ext(const float* y, const int32_t* split, const int32_t* inv_pos,
+                              const float* topk_w, int T, int d, int k, const float* ys,
+                              const int32_t* ys_split, int n_shared, const void* resid,
+                              moe_dtype resid_dt, void* out, moe_dtype out_dt, hipStream_t s);
 
 }  // namespace moe

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: argument checks, workspace carving, kernel launches.
 // Every entry point validates on the host first and enqueues nothing when an
 // argument is rejected. No entry point allocates or frees device memory.
+#include <cmath>
 #include <cstdint>
 
 #include "common.h"
@@ -32,6 +33,31 @@ moe_status check_layer(int T, int d, int ffn, int E, int k, moe_dtype dt) {
 }
 
 bool ok_dtype(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+// Options of the extended forward; T only bounds the shared experts' rows.
+moe_status check_options(const moe_options* o, int T) {
+  if (!o) return MOE_INVALID_ARG;
+  if (!(o->capacity_factor >= 0.f) || !std::isfinite(o->capacity_factor)) return MOE_INVALID_ARG;
+  if (o->norm_weight && (!aligned16(o->norm_weight) || !(o->norm_eps > 0.f) ||
+                         !std::isfinite(o->norm_eps)))
+    return MOE_INVALID_ARG;
+  if (o->n_shared < 0) return MOE_INVALID_ARG;
+  if (o->n_shared > 0) {
+    if (o->shared_ffn < 1 || !ok_ptr(o->shared_gate) || !ok_ptr(o->shared_up) ||
+        !ok_ptr(o->shared_down))
+      return MOE_INVALID_ARG;
+    if (o->n_shared > kMaxShared || o->shared_ffn % 16 != 0) return MOE_UNSUPPORTED;
+    if (static_cast<long long>(T) * o->n_shared >= (1ll << 31)) return MOE_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+// Rows an expert may keep: ceil(cf * T * k / E), or T (no limit) for cf = 0.
+int capacity_rows(float cf, int T, int E, int k) {
+  if (cf == 0.f) return T;
+  const double c = std::ceil(static_cast<double>(cf) * T * k / E);
+  return c >= T ? T : static_cast<int>(c);
+}
 
 }  // namespace
 
@@ -87,7 +113,8 @@ moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* co
   if (!ok_ptr(topk_idx) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(sorted_token) ||
       !ok_ptr(inv_pos))
     return MOE_INVALID_ARG;
-  return launch_permute(topk_idx, T, E, k, counts, offsets, sorted_token, inv_pos, stream);
+  return launch_permute(topk_idx, T, E, k, T, counts, nullptr, offsets, sorted_token, inv_pos,
+                        stream);
 }
 
 size_t moe_router_stats_workspace_size(int T, int E) {
@@ -114,8 +141,8 @@ static moe_status run_experts(const void* x, const int32_t* topk_idx, const floa
                               int d, int ffn, int E, int k, moe_dtype dt, void* out,
                               moe_dtype out_dt, const Workspace& ws, int32_t* counts_out,
                               hipStream_t stream, hipEvent_t* ev) {
-  moe_status st = launch_permute(topk_idx, T, E, k, counts_out ? counts_out : ws.counts,
-                                 ws.offsets, ws.sorted_token, ws.inv_pos, stream);
+  moe_status st = launch_permute(topk_idx, T, E, k, T, counts_out ? counts_out : ws.counts,
+                                 nullptr, ws.offsets, ws.sorted_token, ws.inv_pos, stream);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[2], stream);
   st = launch_gate_up(x, ws.sorted_token, ws.offsets, w_gate, w_up, T, d, ffn, E, k, dt, ws.h,
@@ -193,6 +220,69 @@ moe_status moe_forward_profiled(const void* x, const void* w_router, const void*
   return forward_impl(x, w_router, w_gate, w_up, w_down, router_bias, T, d, ffn, E, k, dt, out,
                       out_dt, logits_out, probs_out, counts_out, ws, ws_bytes, stream,
                       stage_events);
+}
+
+size_t moe_forward_ext_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt,
+                                      const moe_options* opt) {
+  if (check_layer(T, d, ffn, E, k, dt) != MOE_OK || check_options(opt, T) != MOE_OK) return 0;
+  return carve_ext_workspace(nullptr, T, d, ffn, E, k, dt, opt->norm_weight != nullptr,
+                             opt->n_shared, opt->shared_ffn)
+      .bytes;
+}
+
+moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_gate,
+                           const void* w_up, const void* w_down, const float* router_bias, int T,
+                           int d, int ffn, int E, int k, moe_dtype dt, const moe_options* opt,
+                           void* out, moe_dtype out_dt, float* logits_out, float* probs_out,
+                           int32_t* counts_out, int32_t* routed_counts_out, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_layer(T, d, ffn, E, k, dt);
+  if (st != MOE_OK) return st;
+  st = check_options(opt, T);
+  if (st != MOE_OK) return st;
+  if (!ok_dtype(out_dt)) return MOE_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(w_gate) || !ok_ptr(w_up) || !ok_ptr(w_down) ||
+      !ok_ptr(out) || !ok_opt(router_bias) || !ok_opt(logits_out) || !ok_opt(probs_out) ||
+      !ok_opt(counts_out) || !ok_opt(routed_counts_out) || !ok_ptr(ws) ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return MOE_INVALID_ARG;
+  const bool norm = opt->norm_weight != nullptr;
+  const int S = opt->n_shared;
+  const ExtWorkspace w = carve_ext_workspace(ws, T, d, ffn, E, k, dt, norm, S, opt->shared_ffn);
+  if (ws_bytes < w.bytes) return MOE_WORKSPACE_TOO_SMALL;
+  const Workspace& b = w.base;
+  const void* xl = x;
+  if (norm) {
+    st = launch_rms_norm(x, opt->norm_weight, T, d, opt->norm_eps, dt, w.xn, stream);
+    if (st != MOE_OK) return st;
+    xl = w.xn;
+  }
+  st = launch_route(xl, w_router, router_bias, T, d, E, k, dt, logits_out, probs_out, b.topk_idx,
+                    b.topk_w, stream);
+  if (st != MOE_OK) return st;
+  st = launch_permute(b.topk_idx, T, E, k, capacity_rows(opt->capacity_factor, T, E, k),
+                      counts_out ? counts_out : b.counts, routed_counts_out, b.offsets,
+                      b.sorted_token, b.inv_pos, stream);
+  if (st != MOE_OK) return st;
+  st = launch_gate_up(xl, b.sorted_token, b.offsets, w_gate, w_up, T, d, ffn, E, k, dt, b.h,
+                      stream);
+  if (st != MOE_OK) return st;
+  st = launch_down(b.h, b.offsets, w_down, T, d, ffn, E, k, dt, b.y, b.split, stream);
+  if (st != MOE_OK) return st;
+  if (S > 0) {
+    // shared experts: S more experts that every token reaches, T rows each
+    st = launch_identity_rows(T, S, w.st_s, w.off_s, stream);
+    if (st != MOE_OK) return st;
+    st = launch_gate_up(xl, w.st_s, w.off_s, opt->shared_gate, opt->shared_up, T, d,
+                        opt->shared_ffn, S, S, dt, w.h_s, stream);
+    if (st != MOE_OK) return st;
+    st = launch_down(w.h_s, w.off_s, opt->shared_down, T, d, opt->shared_ffn, S, S, dt, w.y_s,
+                     w.split_s, stream);
+    if (st != MOE_OK) return st;
+  }
+  return launch_combine_ext(b.y, b.split, b.inv_pos, b.topk_w, T, d, k, w.y_s, w.split_s, S,
+                            opt->residual ? x : nullptr, dt, out, out_dt, stream);
 }
 
 }  // extern "C"

@@ -17,6 +17,10 @@
 //      the lanes below them; waves are ranked through a per-chunk table of
 //      per-wave counts in LDS; a running base per expert carries the rank
 //      across chunks. Every position is therefore fixed by the input alone.
+// Capacity (KempnerForge moe_capacity_factor): an expert keeps only the
+// assignments of rank < cap (the first cap tokens that chose it); the scan
+// runs over the kept counts, and a dropped assignment gets inv_pos = -1, so
+// the combine adds nothing for it. cap >= T means no limit.
 #include "common.h"
 
 namespace moe {
@@ -26,10 +30,12 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ idx, int n, int E, int k, int nbits, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, int n, int E, int k, int nbits, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ routed_counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_pos) {
   __shared__ int cnt[kMaxExperts];
-  __shared__ int base[kMaxExperts];
+  __shared__ int base[kMaxExperts];   // rank of the expert's next assignment
+  __shared__ int start[kMaxExperts];  // first row of the expert
   __shared__ int wave_cnt[kPermWaves][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -45,7 +51,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      c[q] = e < E ? cnt[e] : 0;
+      c[q] = e < E ? min(cnt[e], cap) : 0;
       s += c[q];
     }
     int incl = s;
@@ -59,9 +65,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
       if (e < E) {
-        base[e] = run;
+        base[e] = 0;
+        start[e] = run;
         offsets[e] = run;
         counts[e] = c[q];
+        if (routed_counts) routed_counts[e] = cnt[e];
       }
       run += c[q];
     }
@@ -84,10 +92,15 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     if (valid && rank == 0) wave_cnt[wave][e] = __popcll(same);
     __syncthreads();
     if (valid) {
-      int pos = base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wave_cnt[w][e];
-      sorted_token[pos] = i / k;
-      inv_pos[i] = pos;
+      int r = base[e] + rank;
+      for (int w = 0; w < wave; ++w) r += wave_cnt[w][e];
+      if (r < cap) {
+        const int pos = start[e] + r;
+        sorted_token[pos] = i / k;
+        inv_pos[i] = pos;
+      } else {
+        inv_pos[i] = -1;
+      }
     } else if (i < n) {
       inv_pos[i] = -1;
     }
@@ -103,13 +116,32 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
 }  // namespace
 
-moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
-                          int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
-                          hipStream_t s) {
+moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int cap, int32_t* counts,
+                          int32_t* routed_counts, int32_t* offsets, int32_t* sorted_token,
+                          int32_t* inv_pos, hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  permute_kernel<<<1, kPermThreads, 0, s>>>(topk_idx, T * k, E, k, nbits, counts, offsets,
-                                            sorted_token, inv_pos);
+  permute_kernel<<<1, kPermThreads, 0, s>>>(topk_idx, T * k, E, k, nbits, cap < T ? cap : T,
+                                            counts, routed_counts, offsets, sorted_token, inv_pos);
+  return launch_status();
+}
+
+namespace {
+// Shared experts take every token: expert s owns rows s*T .. s*T + T-1,
+// row s*T + t holding token t.
+__global__ __launch_bounds__(256) void identity_rows_kernel(int T, int S, int32_t* sorted_token,
+                                                            int32_t* offsets) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < static_cast<size_t>(T) * S) sorted_token[i] = static_cast<int32_t>(i % T);
+  if (i <= static_cast<size_t>(S)) offsets[i] = static_cast<int32_t>(i * T);
+}
+}  // namespace
+
+moe_status launch_identity_rows(int T, int S, int32_t* sorted_token, int32_t* offsets,
+                                hipStream_t s) {
+  const size_t n = static_cast<size_t>(T) * S + 1;
+  identity_rows_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(T, S, sorted_token,
+                                                                             offsets);
   return launch_status();
 }
 

@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"moe_status_string", "moe_workspace_size", "moe_route",
                           "moe_route_logits", "moe_permute", "moe_expert_ffn", "moe_forward",
                           "moe_forward_profiled", "moe_router_stats_workspace_size",
-                          "moe_router_stats"}
+                          "moe_router_stats", "moe_forward_ext_workspace_size", "moe_forward_ext"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -119,6 +119,66 @@ def test_router_stats_validation(L):
     assert L.moe_router_stats(p, p, 10, 8, None, None, p, p, n, None) == INVALID
     assert L.moe_router_stats(p, p, 10, 8, p, ctypes.c_void_p(260), p, p, n, None) == INVALID
     assert L.moe_router_stats(p, p, 1000, 8, p, None, p, p, n - 4, None) == WS_SMALL
+
+
+def test_options_struct_layout(tmp_path):
+    """The ctypes mirror of moe_options has the C struct's size and offsets
+    (compiled from include/moe.h with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"moe.h\"\n"
+        "int main(void) { printf(\"%zu\", sizeof(moe_options));\n"
+        + "".join(f'  printf(" %zu", offsetof(moe_options, {f}));\n'
+                  for f, _ in _lib.MoeOptions._fields_)
+        + "  return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I", _lib.os.path.dirname(_lib.HEADER),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                           text=True).stdout.split()]
+    want = [ctypes.sizeof(_lib.MoeOptions)] + [getattr(_lib.MoeOptions, f).offset
+                                               for f, _ in _lib.MoeOptions._fields_]
+    assert got == want
+
+
+def test_forward_ext_validation(L):
+    p = ctypes.c_void_p(256)
+    o = _lib.MoeOptions()
+    def call(opt=ctypes.byref(o), T=16, ws_bytes=1 << 30):
+        return L.moe_forward_ext(p, p, p, p, p, None, T, 64, 64, 4, 2, BF16, opt, p, F32, None,
+                                 None, None, None, p, ws_bytes, None)
+    assert L.moe_forward_ext_workspace_size(16, 64, 64, 4, 2, BF16, ctypes.byref(o)) == \
+        L.moe_workspace_size(16, 64, 64, 4, 2, BF16)
+    assert call(opt=None) == INVALID
+    o.capacity_factor = -0.5
+    assert call() == INVALID
+    o.capacity_factor = float("nan")
+    assert call() == INVALID
+    o.capacity_factor = 1.25
+    o.norm_weight = 256
+    o.norm_eps = 0.0
+    assert call() == INVALID
+    o.norm_eps = 1e-5
+    o.n_shared = 17
+    o.shared_ffn = 64
+    o.shared_gate = o.shared_up = o.shared_down = 256
+    assert call() == UNSUPPORTED
+    o.n_shared = 2
+    o.shared_ffn = 40
+    assert call() == UNSUPPORTED
+    o.shared_ffn = 64
+    o.shared_down = None
+    assert call() == INVALID
+    o.shared_down = 256
+    need = L.moe_forward_ext_workspace_size(16, 64, 64, 4, 2, BF16, ctypes.byref(o))
+    assert need > L.moe_workspace_size(16, 64, 64, 4, 2, BF16)
+    assert call(ws_bytes=need - 1) == WS_SMALL
+    assert call(T=0) == OK   # nothing to do
 
 
 def test_binding_requires_library(monkeypatch, tmp_path):

@@ -1,0 +1,189 @@
+"""Extended forward (moe_forward_ext) against the oracle's moe_forward with
+the same options: capacity factor, RMSNorm of the input, residual add and
+shared experts, alone and together.
+
+Protocol (as for moe_forward):
+- Routing decisions come from the oracle's own fp64 logits of the layer
+  input (RMSNorm(x) when the norm is on, rounded once to bf16 for bf16
+  layers, as the GPU stores it). The GPU normalises in fp32 before its
+  rounding, so an element whose exact value lies within that fp32 error
+  (taken as 2^-20 relative) of a bf16 rounding midpoint may land on the
+  other neighbour; the logit tolerance adds ulp_i * |W_r[e,i]| for exactly
+  those elements to the usual 1e-5 * sum_i |x_i W_r[e,i]|.
+- Without capacity, a near-tie token may take any valid routing (checked
+  per token). With capacity, one moved assignment can shift which later
+  tokens an expert keeps, so those cases use inputs with no near-ties, and
+  the test asserts that; kept and routed counts must then match exactly.
+- Outputs are compared in fp32 mode on the layer part out - x when the
+  residual is on (x is exact in both), with the tolerance relative to the
+  RMS of that part: 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as wl
+from oracle import moe_oracle as O
+from parity_util import dev_tensor, host, routing_alternatives, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_mixture_experts_renorm_amd as m
+    m.lib()
+    return m
+
+
+def _case(T, d, ffn, E, k, dtype, seed, bias=False, n_shared=0, shared_ffn=0):
+    inp = wl.make_custom_inputs(T, d, ffn, E, dtype, seed=seed, bias=bias)
+    ext = wl.make_block_extras(d, n_shared, shared_ffn, dtype, seed=seed)
+    return inp, ext
+
+
+def _run(M, inp, ext, k, cf, norm, residual, n_shared, eps=1e-5):
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    shared = None
+    if n_shared:
+        shared = (dev_tensor(ext["s_gate"]), dev_tensor(ext["s_up"]), dev_tensor(ext["s_down"]))
+    out, ex = M.moe_forward_ext(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], k,
+                                router_bias=dv["router_bias"], capacity_factor=cf,
+                                norm_weight=dev_tensor(ext["norm_weight"]) if norm else None,
+                                norm_eps=eps, residual=residual, shared=shared,
+                                want_counts=True, want_routed_counts=True)
+    torch.cuda.synchronize()
+    return host(out), {n: host(v) for n, v in ex.items()}
+
+
+def _oracle(inp, ext, k, cf, norm, residual, n_shared, eps=1e-5):
+    shared = (ext["s_gate"], ext["s_up"], ext["s_down"]) if n_shared else None
+    return O.moe_forward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], k,
+                         inp["router_bias"], capacity_factor=cf,
+                         norm_weight=ext["norm_weight"] if norm else None, norm_eps=eps,
+                         residual=residual, shared=shared)
+
+
+def _alternatives(inp, ext, k, norm, bf16, eps=1e-5):
+    wa = np.abs(O.widen(inp["w_router"]))
+    extra = 0.0
+    if norm:
+        x64 = O.rms_norm(inp["x"], ext["norm_weight"], eps)
+        xl = x64
+        if bf16:
+            xl = O.round_to_bf16(x64)
+            _, ex = np.frexp(x64)
+            ulp = np.ldexp(1.0, ex - 8)          # bf16 spacing at |x64|
+            near_mid = (ulp / 2 - np.abs(x64 - xl)) <= 2.0 ** -20 * np.abs(x64)
+            extra = (near_mid * ulp) @ wa.T
+    else:
+        xl = O.widen(inp["x"])
+    L = O.router_logits(xl, inp["w_router"], inp["router_bias"])
+    tol = 1e-5 * (np.abs(xl) @ wa.T) + extra + 1e-30
+    return xl, L, routing_alternatives(L, k, tol)
+
+
+def _token_out(xl, L, probs, t, sel, inp, ext, n_shared):
+    sel = np.array(sel)[np.argsort(-L[t, list(sel)], kind="stable")]
+    pw = probs[t, sel] / probs[t, sel].sum()
+    o = np.zeros(xl.shape[1])
+    for e, we in zip(sel, pw):
+        o += we * O.swiglu_expert(xl[t:t + 1], inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])[0]
+    if n_shared:
+        o += O.shared_experts(xl[t:t + 1], ext["s_gate"], ext["s_up"], ext["s_down"])[0]
+    return o
+
+
+def _compare(got, ref, aux, inp, ext, k, cf, norm, residual, n_shared, bf16):
+    rel = 2e-2 if bf16 else 1e-4
+    xin = O.widen(inp["x"])
+    g = np.asarray(got, np.float64) - (xin if residual else 0.0)
+    r = ref - (xin if residual else 0.0)
+    rms = float(np.sqrt(np.mean(r ** 2)))
+    xl, L, alts = _alternatives(inp, ext, k, norm, bf16)
+    amb = [t for t, a in enumerate(alts) if len(a) > 1]
+    if cf > 0:
+        assert not amb, f"capacity case has {len(amb)} near-tie tokens: pick another seed"
+    err = np.abs(g - r).max(axis=1)
+    bad = [t for t in range(len(r)) if err[t] > rel * rms and t not in amb]
+    assert not bad, f"{len(bad)} tokens off; worst {err.max() / rms:.3e} x RMS (bar {rel})"
+    probs = O.softmax(L)
+    for t in amb:
+        assert any(np.abs(g[t] - _token_out(xl, L, probs, t, s, inp, ext, n_shared)).max()
+                   <= rel * rms for s in alts[t]), f"near-tie token {t} matches no valid routing"
+    return err.max() / rms, len(amb)
+
+
+CAPACITY = [  # T, d, ffn, E, k, dtype, seed, bias, cf
+    (256, 128, 192, 8, 2, "f32", 3, True, 1.0),
+    (300, 256, 320, 8, 2, "bf16", 4, True, 1.25),
+    (128, 64, 96, 4, 1, "f32", 5, False, 0.5),
+    (32, 256, 512, 8, 2, "bf16", 6, True, 1.0),      # few rows per expert: streaming kernels
+    (2048, 1024, 2816, 8, 2, "bf16", 0, True, 1.0),  # the small workload's shape, skewed
+]
+
+
+@pytest.mark.parametrize("T,d,ffn,E,k,dtype,seed,bias,cf", CAPACITY)
+def test_capacity_parity(M, T, d, ffn, E, k, dtype, seed, bias, cf):
+    say(f"ext capacity T={T} d={d} ffn={ffn} E={E} k={k} {dtype} cf={cf}")
+    inp, ext = _case(T, d, ffn, E, k, dtype, seed, bias)
+    got, ex = _run(M, inp, ext, k, cf, False, False, 0)
+    ref, aux = _oracle(inp, ext, k, cf, False, False, 0)
+    cap = O.capacity(T, E, k, cf)
+    assert np.array_equal(ex["routed_counts"], aux["routed_counts"])
+    assert np.array_equal(ex["counts"], aux["counts"])
+    assert ex["counts"].max() <= cap
+    worst, _ = _compare(got, ref, aux, inp, ext, k, cf, False, False, 0, dtype == "bf16")
+    dropped = int(aux["routed_counts"].sum() - aux["counts"].sum())
+    say(f"  cap {cap}: dropped {dropped} of {T * k}; worst {worst:.2e} x RMS")
+
+
+BLOCK = [  # T, d, ffn, E, k, dtype, seed, norm, residual, n_shared, shared_ffn, cf
+    (64, 64, 128, 4, 2, "f32", 11, True, True, 0, 0, 0.0),
+    (200, 256, 320, 8, 2, "bf16", 12, True, True, 0, 0, 0.0),
+    (96, 128, 160, 4, 2, "f32", 13, False, False, 1, 96, 0.0),
+    (150, 256, 192, 8, 2, "bf16", 14, True, True, 2, 320, 0.0),
+    (24, 256, 512, 8, 2, "bf16", 15, True, True, 1, 256, 0.0),      # streaming kernels
+    (2048, 1024, 2816, 8, 2, "bf16", 8, True, True, 1, 2816, 1.25),  # everything at once (seed 8: no near-tie)
+]
+
+
+@pytest.mark.parametrize("T,d,ffn,E,k,dtype,seed,norm,residual,n_shared,shared_ffn,cf", BLOCK)
+def test_block_options_parity(M, T, d, ffn, E, k, dtype, seed, norm, residual, n_shared,
+                              shared_ffn, cf):
+    say(f"ext block T={T} d={d} ffn={ffn} E={E} k={k} {dtype} norm={norm} res={residual} "
+        f"shared={n_shared}x{shared_ffn} cf={cf}")
+    inp, ext = _case(T, d, ffn, E, k, dtype, seed, False, n_shared, shared_ffn)
+    got, ex = _run(M, inp, ext, k, cf, norm, residual, n_shared)
+    ref, aux = _oracle(inp, ext, k, cf, norm, residual, n_shared)
+    worst, amb = _compare(got, ref, aux, inp, ext, k, cf, norm, residual, n_shared,
+                          dtype == "bf16")
+    say(f"  worst {worst:.2e} x RMS, near-ties {amb}")
+
+
+def test_options_off_equals_moe_forward(M):
+    """With every option off the extended forward runs the same kernels as
+    moe_forward and must give bit-identical results."""
+    w = wl.WORKLOADS["small"]
+    inp = wl.make_layer_inputs(w, seed=0)
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    a = M.moe_forward(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k,
+                      router_bias=dv["router_bias"])
+    b = M.moe_forward_ext(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k,
+                          router_bias=dv["router_bias"])
+    assert torch.equal(a, b)
+
+
+def test_ext_deterministic_and_zero_tokens(M):
+    inp, ext = _case(150, 256, 192, 8, 2, "bf16", 14, False, 2, 320)
+    a, _ = _run(M, inp, ext, 2, 1.25, True, True, 2)
+    b, _ = _run(M, inp, ext, 2, 1.25, True, True, 2)
+    assert np.array_equal(a, b)
+    x = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    wr = torch.zeros((4, 64), device="cuda")
+    wg = torch.zeros((4, 32, 64), device="cuda")
+    wd = torch.zeros((4, 64, 32), device="cuda")
+    out = M.moe_forward_ext(x, wr, wg, wg, wd, 2, capacity_factor=1.0,
+                            norm_weight=torch.ones(64, device="cuda"), residual=True)
+    assert out.shape == (0, 64)

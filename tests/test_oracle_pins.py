@@ -357,6 +357,16 @@ def pin_rms_norm_library():
                                rtol=1e-12)
 
 
+def pin_round_to_bf16():
+    """Rounding to bf16 equals torch's float32 -> bfloat16 conversion on
+    float32 values (one rounding either way), and ties go to even."""
+    a = (_rand((4000,), 51) * np.exp(_rand((4000,), 52) * 4.0)).astype(np.float32)
+    want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to_bf16(a.astype(np.float64)), want)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(2 + 2.0 ** -7), 0.0, 2.0 ** -130 * 0])
+    assert list(O.round_to_bf16(ties)) == [1.0, 1 + 2.0 ** -6, -2.0, 0.0, 0.0]
+
+
 def pin_residual_and_shared():
     """With W_down = 0 the block returns its input exactly; shared experts
     add torch's SwiGLU of the normalised input; the residual is the
@@ -503,6 +513,12 @@ def _m_offsets_inclusive(idx, E):
 
 _REAL = {"permute": O.permute}
 
+def _m_round_half_up(a):
+    a = np.asarray(a, np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.floor(m * 256.0 + 0.5) / 256.0, e)
+
+
 _orig_capacity, _orig_permute, _orig_rms, _orig_shared, _orig_ffn = (
     O.capacity, O.permute, O.rms_norm, O.shared_experts, O.expert_ffn)
 
@@ -548,6 +564,7 @@ MUTANTS = {
     "rms_eps_outside_root": ("rms_norm", _m_rms_eps_outside),
     "shared_half_weight": ("shared_experts", _m_shared_half),
     "ffn_ignores_capacity": ("expert_ffn", _m_ffn_ignores_cap),
+    "bf16_round_half_up": ("round_to_bf16", _m_round_half_up),
     "no_renormalisation": ("renormalise", _m_no_renorm),
     "gate_sum_combine": ("combine", _m_gate_sum_combine),
     "silu_on_up": ("swiglu_expert", _m_silu_on_up),
