@@ -13,7 +13,14 @@ Prints one JSON line: tokens/s for the layer, plus
                   with HIP events recorded between the layer's kernels on its
                   stream, against the bf16 dense MFMA peak (prefill-like
                   workloads) or its algorithmic bytes against HBM (decode);
-  cpu_baseline -- the CPU oracle timed on this host on a bounded token sample.
+  cpu_baseline -- the CPU oracle timed on this host on a bounded token sample;
+  extras       -- the calls beyond the layer itself, timed the same way on the
+                  same inputs: moe_router_stats on the layer's probabilities
+                  and counts (bytes read against HBM), and moe_forward_ext
+                  with each block option (capacity factor 1.25; RMSNorm and
+                  residual; one shared expert of the routed experts' width;
+                  all together), each as a whole-layer step against the
+                  layer's bound (active FLOPs, or bytes for decode).
 """
 import argparse
 import json
@@ -28,6 +35,38 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE layer tokens/sec + % bf16 MFMA peak (active FLOPs), d4096/ffn14336/E8/top2"
 CPU_SAMPLE = {"tiny": 64, "small": 2048, "prefill": 4096, "decode": 32, "skewed": 8192}
+COPY_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {  # the files whose text defines each dominant kernel
+    "expert_gemm_bf16_kernel": ["expert_gemm.hip", "common.h"],
+    "expert_stream_kernel": ["expert_stream.hip", "common.h"],
+}
+
+
+def source_sha256(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_renorm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's
+    reading for a plain copy of known size), or None when there are none for
+    this workload or the kernel's source has changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = t.get("kernels", {}).get(workload)
+    if not r or r.get("source_sha256") != source_sha256(kernel):
+        return None
+    c = t["calibration"]
+    return (r["fetch_kib"] * 1024 * c["fetch_scale"] + r["write_kib"] * 1024 * c["write_scale"])
 
 
 def log(msg):
@@ -44,6 +83,11 @@ def main():
                     choices=["tiny", "small", "prefill", "decode", "skewed"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the router-statistics and block-option timings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -53,6 +97,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = COPY_BYTES // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
+        return
 
     import moe_workloads as wl
     import sparse_mixture_experts_renorm_amd as moe
@@ -113,14 +167,18 @@ def main():
     gu_bytes = touched * 2 * w.ffn * w.d * 2 + rows * w.d * 2 + rows * w.ffn * 2
     gu_s = stage_ms["gate_up"] / 1e3
     if rows > 32 * w.E:   # tiled MFMA kernels (the library's own switch)
-        roof = {"kernel": "expert_gemm_bf16_kernel<true>", "bound": "mfma",
+        kern = "expert_gemm_bf16_kernel"
+        roof = {"kernel": "expert_gemm_bf16_kernel<true, 8>", "bound": "mfma",
                 "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:                   # weight-streaming kernels
-        roof = {"kernel": "expert_stream_kernel<true>", "bound": "hbm",
+        kern = "expert_stream_kernel"
+        nb = 1 if rows <= 16 * w.E else 2
+        roof = {"kernel": f"expert_stream_kernel<true, 1, {nb}>", "bound": "hbm",
                 "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["mean_ms"] = stage_ms["gate_up"]
-    roof["traffic"] = None
+    roof["algorithmic_per_launch"] = gu_flops if roof["bound"] == "mfma" else gu_bytes
+    roof["traffic"] = measured_traffic(w.name, kern)
 
     active = w.active_flops
     layer_s = ms_per_step / 1e3
@@ -147,6 +205,9 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_extras:
+        result["extras"] = extras(args, w, moe, wl, dv, lay, call, to_dev, log)
+
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
         S = min(w.T, CPU_SAMPLE[w.name])
@@ -165,6 +226,63 @@ def main():
             "sample": f"first {S} of the {w.T} tokens of the same seeded workload, fp64 numpy "
                       f"oracle, all experts' weights widened, {dt:.1f}s"}
     print(json.dumps(result), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def extras(args, w, moe, wl, dv, lay, call, to_dev, log):
+    """Timings of the calls beyond the plain layer (see the module docstring)."""
+    import numpy as np
+    steps, warm = max(1, min(args.steps, 10)), max(1, min(args.warmup, 3))
+    out = {}
+    _, ex = moe.moe_forward(*lay, **call, want_probs=True, want_counts=True)
+    probs, counts = ex["probs"], ex["counts"]
+    ms = _timed(lambda: moe.moe_router_stats(probs, counts), steps, warm)
+    nbytes = w.T * w.E * 4 + w.E * 4
+    out["router_stats"] = {"ms": ms, "bytes": nbytes, "GB/s": nbytes / ms / 1e6,
+                           "hbm_frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+    log("block options: generating the norm weight and one shared expert")
+    blk = wl.make_block_extras(w.d, 1, w.ffn, w.dtype, seed=0)
+    g = to_dev(blk["norm_weight"])
+    shared = (to_dev(blk["s_gate"]), to_dev(blk["s_up"]), to_dev(blk["s_down"]))
+    es = 2 if w.dtype == "bf16" else 4
+    variants = {
+        "capacity_1.25": dict(capacity_factor=1.25),
+        "rmsnorm_residual": dict(norm_weight=g, residual=True),
+        f"shared_1x{w.ffn}": dict(shared=shared),
+        "all_options": dict(capacity_factor=1.25, norm_weight=g, residual=True, shared=shared),
+    }
+    import torch
+    ext_out = call["out"]
+    for name, opt in variants.items():
+        n = moe.moe_forward_ext_workspace_size(w.T, w.d, w.ffn, w.E, w.k, dv["x"].dtype, **opt)
+        wsb = torch.empty(n + 256, dtype=torch.uint8, device=dv["x"].device)
+        kw = dict(router_bias=dv["router_bias"], out=ext_out, ws=wsb, **opt)
+        _, ex = moe.moe_forward_ext(*lay, **kw, want_counts=True)
+        kept = ex["counts"].cpu().numpy().astype(np.int64)
+        ms = _timed(lambda: moe.moe_forward_ext(*lay, **kw), steps, warm)
+        n_sh = 1 if "shared" in opt else 0
+        flops = (6.0 * kept.sum() * w.d * w.ffn + 2.0 * w.T * w.d * w.E
+                 + n_sh * 6.0 * w.T * w.d * w.ffn)
+        wbytes = (np.count_nonzero(kept) + n_sh) * 3.0 * w.d * w.ffn * es
+        r = {"ms": ms, "tokens/s": w.T / ms * 1e3, "kept_rows": int(kept.sum()),
+             "active_tflops": flops / ms / 1e9, "mfma_peak_frac": flops / ms / 1e9 / PEAK_BF16_TFLOPS,
+             "weight_GB/s": wbytes / ms / 1e6, "hbm_frac": wbytes / ms / 1e6 / PEAK_HBM_GBS}
+        out[name] = r
+        log(f"{name}: {ms:.3f} ms")
+    return out
 
 
 if __name__ == "__main__":
