@@ -43,12 +43,26 @@ KERNEL_SOURCES = {  # the files whose text defines each dominant kernel
 }
 
 
-def source_sha256(kernel: str) -> str:
+def code_text(text: str) -> str:
+    """Source text without comments and blank space, so that only a change
+    of the code itself changes its hash."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def source_sha256(kernel: str, read=None) -> str:
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "sparse_mixture_experts_renorm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        path = os.path.join("sparse_mixture_experts_renorm_amd", "csrc", f)
+        if read is None:
+            with open(os.path.join(ROOT, path)) as fh:
+                text = fh.read()
+        else:
+            text = read(path)
+        h.update(code_text(text).encode())
     return h.hexdigest()
 
 

@@ -10,16 +10,19 @@
 // because rounding y to bf16 as well would spend about half of the 2e-2 x RMS
 // error budget of bf16 workloads on top of h's rounding.
 //
-// bf16 path (gfx950). One workgroup of 4 waves per CU computes a 256 x 256
-// tile: 256 permuted rows against 256 weight rows (gate/up: 128 gate rows and
-// the same 128 up rows, giving 128 columns of h; down: 256 columns of y).
-// Each wave owns a 128 x 128 quarter: 16 accumulators of
-// v_mfma_f32_32x32x16_bf16 (256 fp32 per lane, held in AGPRs), so every
-// 16-byte fragment read from LDS feeds 4 MFMAs. The reduction dimension moves
+// bf16 path (gfx950). One workgroup of 8 waves per CU (two per SIMD)
+// computes a 256 x 256 tile: 256 permuted rows against 256 weight rows
+// (gate/up: 128 gate rows and the same 128 up rows, giving 128 columns of h;
+// down: 256 columns of y). Each wave owns a 128 x 64 part: 8 accumulators of
+// v_mfma_f32_32x32x16_bf16 (128 fp32 per lane), so each 16-byte fragment read
+// from LDS feeds 2 or 4 MFMAs; with two waves per SIMD one wave's MFMAs run
+// while the other waits to issue its loads. The reduction dimension moves
 // in steps of 64 through two LDS stages (64 KB each): the loads of step s+1
 // are issued with global_load_lds_dwordx4 (memory to LDS without VGPRs) just
-// before the MFMAs of step s. Each lane supplies its own address, which is how the token gather
-// of the gate/up pass is done; lanes past K read a 16-byte zero page.
+// before the MFMAs of step s. Each lane supplies its own address, which is
+// how the token gather of the gate/up pass is done; lanes past K read a
+// 16-byte zero page. The step time is set by the bytes each CU must move
+// from L2 per step (64 KB per 8.4 MFLOP), not by the LDS or the MFMAs.
 // LDS rows are 128 bytes (64 bf16); chunk c (16 bytes) of row r is stored at
 // slot c ^ ((r >> 1) & 7). gfx950 serves a 16-byte-per-lane LDS read 16 lanes
 // at a time over 64 four-byte banks; a fragment read sends 16 consecutive
