@@ -99,6 +99,8 @@ def main():
                     help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router-statistics and block-option timings")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the timing of the layer call replayed from a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -218,6 +220,24 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+
+    if not args.no_graph:
+        # the same call captured once into a HIP graph and replayed: the
+        # kernels are identical, only the launches are batched
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            moe.moe_forward(*lay, **call)          # warm the caching allocator on this stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s_cap):
+                moe.moe_forward(*lay, **call)
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        gms = _timed(g.replay, args.steps, args.warmup)
+        result["graph"] = {"ms_per_step": gms, "tokens/s": w.T / gms * 1e3,
+                           "note": "same layer call replayed from a captured HIP graph"}
+        log(f"graph replay: {gms:.3f} ms/step")
 
     if not args.no_extras:
         result["extras"] = extras(args, w, moe, wl, dv, lay, call, to_dev, log)
