@@ -100,10 +100,14 @@ moe_status moe_route_logits(const float* logits, int T, int E, int k,
  *   each permuted row, experts in ascending order and, within an expert,
  *   tokens in ascending order; inv_pos [T*k]: the row of assignment t*k+j.
  * All integer; bit-exact. Source: axonml-nn MoELayer::forward (utilisation
- * counts; per-expert token lists gathered in token order). */
+ * counts; per-expert token lists gathered in token order).
+ * ws: caller scratch of moe_permute_workspace_size(T, E, k) bytes (per-block
+ * expert histograms when T*k is large; the size is 0, and ws may be NULL,
+ * when one workgroup does the whole job). WORKSPACE_TOO_SMALL below it. */
+size_t moe_permute_workspace_size(int T, int E, int k);
 moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k,
                        int32_t* counts, int32_t* offsets, int32_t* sorted_token,
-                       int32_t* inv_pos, hipStream_t stream);
+                       int32_t* inv_pos, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The expert half of the layer for a given routing: permute, per-expert
  * SwiGLU h = SiLU(X W_g^T) * (X W_u^T), y = h W_d^T, and the weighted combine

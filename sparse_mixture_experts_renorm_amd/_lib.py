@@ -52,7 +52,8 @@ def lib() -> ctypes.CDLL:
         _p("moe_workspace_size", sz, i, i, i, i, i, i)
         _p("moe_route", i, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp)
         _p("moe_route_logits", i, vp, i, i, i, vp, vp, vp, vp)
-        _p("moe_permute", i, vp, i, i, i, vp, vp, vp, vp, vp)
+        _p("moe_permute_workspace_size", sz, i, i, i)
+        _p("moe_permute", i, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp)
         _p("moe_expert_ffn", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, sz, vp)
         _p("moe_forward", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp, vp, sz, vp)
         _p("moe_forward_profiled", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp,
@@ -167,8 +168,11 @@ def moe_permute(topk_idx, E, stream=None):
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     st = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    n = int(lib().moe_permute_workspace_size(T, E, k))
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=dev) if n else None
+    wp, wn = _ws_ptr(ws) if n else (None, 0)
     _check(lib().moe_permute(_ptr(topk_idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(st),
-                             _ptr(inv), _stream(stream)), "moe_permute")
+                             _ptr(inv), wp, wn, _stream(stream)), "moe_permute")
     return counts, offsets, st, inv
 
 

@@ -12,6 +12,8 @@ constexpr int kWave = 64;         // CDNA wavefront width
 constexpr int kMaxExperts = 256;  // library limit on E
 constexpr int kMaxTopK = 16;      // library limit on k
 constexpr int kMaxDownSplit = 4;  // most parts the down GEMM's reduction is cut into
+constexpr int kPermMaxBlocks = 256;            // most workgroups of the permutation
+constexpr long long kPermBlockedFrom = 4096;   // up to this many assignments: one workgroup
 
 typedef uint16_t bf16_t;          // bfloat16 storage (bit pattern)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -52,6 +54,7 @@ struct Workspace {
   void* h;                // [T*k, ffn] in dt
   float* y;               // [kMaxDownSplit, T*k, d] fp32 partial sums of the down GEMM
   int32_t* split;         // [1] number of partial sums in y
+  int32_t* block_counts;  // [kPermMaxBlocks * E] per-block expert histograms of the permutation
   size_t bytes;
 };
 
@@ -73,6 +76,7 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   w.h = take(tk * static_cast<size_t>(ffn) * es);
   w.y = reinterpret_cast<float*>(take(kMaxDownSplit * tk * static_cast<size_t>(d) * 4));
   w.split = reinterpret_cast<int32_t*>(take(4));
+  w.block_counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(kPermMaxBlocks) * E * 4));
   w.bytes = off;
   return w;
 }
@@ -119,9 +123,12 @@ moe_status launch_route(const void* x, const void* w_router, const float* bias, 
 moe_status launch_route_logits(const float* logits, int T, int E, int k, float* probs,
                                int32_t* topk_idx, float* topk_w, hipStream_t s);
 // cap: most rows an expert keeps (>= T: no limit); routed_counts may be null.
+// block_counts: [permute_blocks(T, k) * E] scratch, unused (may be null)
+// when permute_blocks(T, k) == 0 (one workgroup does everything).
+int permute_blocks(int T, int k);
 moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int cap, int32_t* counts,
                           int32_t* routed_counts, int32_t* offsets, int32_t* sorted_token,
-                          int32_t* inv_pos, hipStream_t s);
+                          int32_t* inv_pos, int32_t* block_counts, hipStream_t s);
 // S shared experts over all T tokens: rows s*T + t hold token t.
 moe_status launch_identity_rows(int T, int S, int32_t* sorted_token, int32_t* offsets,
                                 hipStream_t s);

@@ -104,17 +104,25 @@ moe_status moe_route(const void* x, const void* w_router, const float* router_bi
                       stream);
 }
 
+size_t moe_permute_workspace_size(int T, int E, int k) {
+  if (check_routing(T, E, k) != MOE_OK) return 0;
+  return static_cast<size_t>(permute_blocks(T, k)) * E * sizeof(int32_t);
+}
+
 moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
-                       int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
-                       hipStream_t stream) {
+                       int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_routing(T, E, k);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(topk_idx) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(sorted_token) ||
       !ok_ptr(inv_pos))
     return MOE_INVALID_ARG;
+  const size_t need = moe_permute_workspace_size(T, E, k);
+  if (need > 0 && !ok_ptr(ws)) return MOE_INVALID_ARG;
+  if (ws_bytes < need) return MOE_WORKSPACE_TOO_SMALL;
   return launch_permute(topk_idx, T, E, k, T, counts, nullptr, offsets, sorted_token, inv_pos,
-                        stream);
+                        static_cast<int32_t*>(ws), stream);
 }
 
 size_t moe_router_stats_workspace_size(int T, int E) {
@@ -142,7 +150,8 @@ static moe_status run_experts(const void* x, const int32_t* topk_idx, const floa
                               moe_dtype out_dt, const Workspace& ws, int32_t* counts_out,
                               hipStream_t stream, hipEvent_t* ev) {
   moe_status st = launch_permute(topk_idx, T, E, k, T, counts_out ? counts_out : ws.counts,
-                                 nullptr, ws.offsets, ws.sorted_token, ws.inv_pos, stream);
+                                 nullptr, ws.offsets, ws.sorted_token, ws.inv_pos,
+                                 ws.block_counts, stream);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[2], stream);
   st = launch_gate_up(x, ws.sorted_token, ws.offsets, w_gate, w_up, T, d, ffn, E, k, dt, ws.h,
@@ -263,7 +272,7 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
   if (st != MOE_OK) return st;
   st = launch_permute(b.topk_idx, T, E, k, capacity_rows(opt->capacity_factor, T, E, k),
                       counts_out ? counts_out : b.counts, routed_counts_out, b.offsets,
-                      b.sorted_token, b.inv_pos, stream);
+                      b.sorted_token, b.inv_pos, b.block_counts, stream);
   if (st != MOE_OK) return st;
   st = launch_gate_up(xl, b.sorted_token, b.offsets, w_gate, w_up, T, d, ffn, E, k, dt, b.h,
                       stream);

@@ -7,8 +7,8 @@
 // Assignment i = t*k + j is ordered by i, which within one expert is token
 // order because a token chooses an expert at most once.
 //
-// One workgroup of 16 waves does the whole job (T*k is at most a few
-// hundred thousand here, and the kernel is latency-bound):
+// Up to kPermBlockedFrom assignments one workgroup of 16 waves does the
+// whole job in one launch (the call is latency-bound there):
 //   1. histogram of the expert ids with integer LDS atomics (exact, so the
 //      order of the atomics does not matter),
 //   2. exclusive scan of the E counts by one wave (shuffle scan),
@@ -17,6 +17,9 @@
 //      the lanes below them; waves are ranked through a per-chunk table of
 //      per-wave counts in LDS; a running base per expert carries the rank
 //      across chunks. Every position is therefore fixed by the input alone.
+// Above that, a count pass writes each block's expert histogram and a
+// scatter pass lets every block derive the global offsets and its own rank
+// bases from that table, then run step 3 on its range of assignments.
 // Capacity (KempnerForge moe_capacity_factor): an expert keeps only the
 // assignments of rank < cap (the first cap tokens that chose it); the scan
 // runs over the kept counts, and a dropped assignment gets inv_pos = -1, so
@@ -29,24 +32,15 @@ namespace {
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ idx, int n, int E, int k, int nbits, int cap,
-    int32_t* __restrict__ counts, int32_t* __restrict__ routed_counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_pos) {
-  __shared__ int cnt[kMaxExperts];
-  __shared__ int base[kMaxExperts];   // rank of the expert's next assignment
-  __shared__ int start[kMaxExperts];  // first row of the expert
-  __shared__ int wave_cnt[kPermWaves][kMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  for (int e = tid; e < E; e += kPermThreads) cnt[e] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += kPermThreads) {
-    const int e = idx[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  if (wave == 0) {
+// Wave 0 scans the kept counts min(cnt[e], cap) into start[] (first row of
+// each expert); with `publish` it also writes offsets, counts and the routed
+// counts. Called by every thread of the block.
+__device__ __forceinline__ void scan_experts(const int* cnt, int E, int cap, bool publish,
+                                             int* start, int32_t* __restrict__ counts,
+                                             int32_t* __restrict__ routed_counts,
+                                             int32_t* __restrict__ offsets) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < kWave) {
     int c[4], s = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -65,22 +59,36 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
       if (e < E) {
-        base[e] = 0;
         start[e] = run;
-        offsets[e] = run;
-        counts[e] = c[q];
-        if (routed_counts) routed_counts[e] = cnt[e];
+        if (publish) {
+          offsets[e] = run;
+          counts[e] = c[q];
+          if (routed_counts) routed_counts[e] = cnt[e];
+        }
       }
       run += c[q];
     }
-    if (lane == kWave - 1) offsets[E] = incl;
+    if (publish && lane == kWave - 1) offsets[E] = incl;
   }
+  __syncthreads();
+}
+
+// Assignments [c_begin, c_end) in chunks of 1024, in order. base[e] holds
+// the rank (among all assignments to e, in assignment order) of the next
+// one to e and is advanced chunk by chunk; rank r < cap lands in row
+// start[e] + r, others are dropped (inv_pos = -1). Called by every thread.
+__device__ __forceinline__ void rank_chunks(const int32_t* __restrict__ idx, int c_begin,
+                                            int c_end, int E, int k, int nbits, int cap, int* base,
+                                            const int* start, int (*wave_cnt)[kMaxExperts],
+                                            int32_t* __restrict__ sorted_token,
+                                            int32_t* __restrict__ inv_pos) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int c0 = 0; c0 < n; c0 += kPermThreads) {
+  for (int c0 = c_begin; c0 < c_end; c0 += kPermThreads) {
     for (int q = tid; q < kPermWaves * E; q += kPermThreads) wave_cnt[q / E][q % E] = 0;
     __syncthreads();
     const int i = c0 + tid;
-    int e = i < n ? idx[i] : -1;
+    int e = i < c_end ? idx[i] : -1;
     const bool valid = e >= 0 && e < E;
     uint64_t same = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
@@ -101,7 +109,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       } else {
         inv_pos[i] = -1;
       }
-    } else if (i < n) {
+    } else if (i < c_end) {
       inv_pos[i] = -1;
     }
     __syncthreads();
@@ -114,15 +122,108 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
 }
 
+// One workgroup for everything (few assignments: one launch).
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ idx, int n, int E, int k, int nbits, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ routed_counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_pos) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int start[kMaxExperts];
+  __shared__ int wave_cnt[kPermWaves][kMaxExperts];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPermThreads) {
+    cnt[e] = 0;
+    base[e] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kPermThreads) {
+    const int e = idx[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  scan_experts(cnt, E, cap, true, start, counts, routed_counts, offsets);
+  rank_chunks(idx, 0, n, E, k, nbits, cap, base, start, wave_cnt, sorted_token, inv_pos);
+}
+
+// Many assignments: block b owns assignments [b*C, (b+1)*C) (C a multiple
+// of 1024). Pass 1 writes each block's expert histogram; pass 2 gives every
+// block the totals and, from the blocks before it, the rank base of each
+// expert, so each block scatters its own range in order.
+__global__ __launch_bounds__(kPermThreads) void permute_count_kernel(
+    const int32_t* __restrict__ idx, int n, int E, int C, int32_t* __restrict__ block_counts) {
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPermThreads) cnt[e] = 0;
+  __syncthreads();
+  const int c_begin = blockIdx.x * C, c_end = min(n, c_begin + C);
+  for (int i = c_begin + tid; i < c_end; i += kPermThreads) {
+    const int e = idx[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermThreads)
+    block_counts[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ idx, int n, int E, int k, int nbits, int cap, int C,
+    const int32_t* __restrict__ block_counts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ routed_counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_pos) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int start[kMaxExperts];
+  __shared__ int wave_cnt[kPermWaves][kMaxExperts];
+  const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
+  for (int e = tid; e < E; e += kPermThreads) {
+    int tot = 0, pre = 0;
+    for (int bb = 0; bb < nb; ++bb) {
+      const int c = block_counts[static_cast<size_t>(bb) * E + e];
+      pre += bb < b ? c : 0;
+      tot += c;
+    }
+    cnt[e] = tot;
+    base[e] = pre;
+  }
+  __syncthreads();
+  scan_experts(cnt, E, cap, b == 0, start, counts, routed_counts, offsets);
+  const int c_begin = b * C;
+  rank_chunks(idx, c_begin, min(n, c_begin + C), E, k, nbits, cap, base, start, wave_cnt,
+              sorted_token, inv_pos);
+}
+
 }  // namespace
+
+int permute_blocks(int T, int k) {
+  const long long n = static_cast<long long>(T) * k;
+  if (n <= kPermBlockedFrom) return 0;  // one workgroup
+  const long long chunks = (n + kPermThreads - 1) / kPermThreads;
+  const long long per = (chunks + kPermMaxBlocks - 1) / kPermMaxBlocks;  // chunks per block
+  return static_cast<int>((chunks + per - 1) / per);
+}
 
 moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int cap, int32_t* counts,
                           int32_t* routed_counts, int32_t* offsets, int32_t* sorted_token,
-                          int32_t* inv_pos, hipStream_t s) {
+                          int32_t* inv_pos, int32_t* block_counts, hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  permute_kernel<<<1, kPermThreads, 0, s>>>(topk_idx, T * k, E, k, nbits, cap < T ? cap : T,
-                                            counts, routed_counts, offsets, sorted_token, inv_pos);
+  const int n = T * k;
+  const int c = cap < T ? cap : T;
+  const int nb = permute_blocks(T, k);
+  if (nb == 0) {
+    permute_kernel<<<1, kPermThreads, 0, s>>>(topk_idx, n, E, k, nbits, c, counts, routed_counts,
+                                              offsets, sorted_token, inv_pos);
+    return launch_status();
+  }
+  const long long chunks = (static_cast<long long>(n) + kPermThreads - 1) / kPermThreads;
+  const int C = static_cast<int>((chunks + nb - 1) / nb) * kPermThreads;
+  permute_count_kernel<<<nb, kPermThreads, 0, s>>>(topk_idx, n, E, C, block_counts);
+  moe_status st = launch_status();
+  if (st != MOE_OK) return st;
+  permute_scatter_kernel<<<nb, kPermThreads, 0, s>>>(topk_idx, n, E, k, nbits, c, C, block_counts,
+                                                     counts, routed_counts, offsets, sorted_token,
+                                                     inv_pos);
   return launch_status();
 }
 

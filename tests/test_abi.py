@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"moe_status_string", "moe_workspace_size", "moe_route",
                           "moe_route_logits", "moe_permute", "moe_expert_ffn", "moe_forward",
                           "moe_forward_profiled", "moe_router_stats_workspace_size",
-                          "moe_router_stats", "moe_forward_ext_workspace_size", "moe_forward_ext"}
+                          "moe_router_stats", "moe_forward_ext_workspace_size", "moe_forward_ext",
+                          "moe_permute_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -95,9 +96,15 @@ def test_expert_ffn_and_permute_validation(L):
     p = ctypes.c_void_p(256)
     assert L.moe_expert_ffn(p, p, p, p, p, p, 8, 64, 64, 4, 5, BF16, p, F32, p, 1 << 30, None) == INVALID
     assert L.moe_expert_ffn(p, p, p, p, p, p, 8, 64, 64, 4, 2, BF16, p, F32, p, 10, None) == WS_SMALL
-    assert L.moe_permute(p, 8, 4, 5, p, p, p, p, None) == INVALID
-    assert L.moe_permute(p, 8, 257, 2, p, p, p, p, None) == UNSUPPORTED
-    assert L.moe_permute(None, 8, 4, 2, p, p, p, p, None) == INVALID
+    assert L.moe_permute(p, 8, 4, 5, p, p, p, p, None, 0, None) == INVALID
+    assert L.moe_permute(p, 8, 257, 2, p, p, p, p, None, 0, None) == UNSUPPORTED
+    assert L.moe_permute(None, 8, 4, 2, p, p, p, p, None, 0, None) == INVALID
+    # one workgroup up to 4096 assignments (no scratch), then per-block histograms
+    assert L.moe_permute_workspace_size(2048, 8, 2) == 0
+    assert L.moe_permute_workspace_size(8192, 64, 8) == 64 * 64 * 4
+    assert L.moe_permute_workspace_size(1 << 20, 8, 2) == 256 * 8 * 4
+    assert L.moe_permute(p, 8192, 64, 8, p, p, p, p, None, 0, None) == INVALID
+    assert L.moe_permute(p, 8192, 64, 8, p, p, p, p, p, 64 * 64 * 4 - 1, None) == WS_SMALL
     assert L.moe_route(p, p, None, 8, 40, 4, 2, BF16, None, None, p, p, None) == UNSUPPORTED
     ev = (ctypes.c_void_p * 6)(*([16] * 5 + [0]))
     assert L.moe_forward_profiled(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, p, F32, None, None,

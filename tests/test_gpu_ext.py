@@ -121,6 +121,7 @@ CAPACITY = [  # T, d, ffn, E, k, dtype, seed, bias, cf
     (128, 64, 96, 4, 1, "f32", 5, False, 0.5),
     (32, 256, 512, 8, 2, "bf16", 6, True, 1.0),      # few rows per expert: streaming kernels
     (2048, 1024, 2816, 8, 2, "bf16", 0, True, 1.0),  # the small workload's shape, skewed
+    (3000, 256, 320, 8, 2, "bf16", 20, True, 1.0),   # 6000 assignments: multi-block permutation
 ]
 
 
