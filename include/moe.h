@@ -32,7 +32,9 @@
  *   - Non-finite inputs are outside the contract (the page's sort cannot
  *     order NaN); they are not detected on the device.
  *   - Limits (MOE_UNSUPPORTED beyond them): E <= 256, k <= 16,
- *     d % 16 == 0, ffn % 16 == 0, T * k < 2^31.
+ *     d % 16 == 0, ffn % 16 == 0, T * k < 2^31, and in bytes of the storage
+ *     dtype T*d, T*k*ffn and ffn*d below 2^32 (the GEMM kernels address x,
+ *     the hidden activations and one expert's weights with 32-bit offsets).
  *   - Results are deterministic: no floating-point atomics are used, so two
  *     calls on the same inputs give bit-identical outputs.
  */

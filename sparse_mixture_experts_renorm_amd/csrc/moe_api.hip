@@ -29,13 +29,20 @@ moe_status check_layer(int T, int d, int ffn, int E, int k, moe_dtype dt) {
   if (st != MOE_OK) return st;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_UNSUPPORTED;
   if (d % 16 != 0 || ffn % 16 != 0) return MOE_UNSUPPORTED;
+  // the tiled kernels address x, h and one expert's weights with 32-bit
+  // byte offsets
+  const long long es = dt == MOE_BF16 ? 2 : 4;
+  const long long lim = 1ll << 32;
+  if (static_cast<long long>(T) * d * es >= lim || static_cast<long long>(T) * k * ffn * es >= lim ||
+      static_cast<long long>(ffn) * d * es >= lim)
+    return MOE_UNSUPPORTED;
   return MOE_OK;
 }
 
 bool ok_dtype(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 
 // Options of the extended forward; T only bounds the shared experts' rows.
-moe_status check_options(const moe_options* o, int T) {
+moe_status check_options(const moe_options* o, int T, moe_dtype dt) {
   if (!o) return MOE_INVALID_ARG;
   if (!(o->capacity_factor >= 0.f) || !std::isfinite(o->capacity_factor)) return MOE_INVALID_ARG;
   if (o->norm_weight && (!aligned16(o->norm_weight) || !(o->norm_eps > 0.f) ||
@@ -48,6 +55,9 @@ moe_status check_options(const moe_options* o, int T) {
       return MOE_INVALID_ARG;
     if (o->n_shared > kMaxShared || o->shared_ffn % 16 != 0) return MOE_UNSUPPORTED;
     if (static_cast<long long>(T) * o->n_shared >= (1ll << 31)) return MOE_UNSUPPORTED;
+    const long long es = dt == MOE_BF16 ? 2 : 4;
+    if (static_cast<long long>(T) * o->n_shared * o->shared_ffn * es >= (1ll << 32))
+      return MOE_UNSUPPORTED;
   }
   return MOE_OK;
 }
@@ -233,7 +243,7 @@ moe_status moe_forward_profiled(const void* x, const void* w_router, const void*
 
 size_t moe_forward_ext_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt,
                                       const moe_options* opt) {
-  if (check_layer(T, d, ffn, E, k, dt) != MOE_OK || check_options(opt, T) != MOE_OK) return 0;
+  if (check_layer(T, d, ffn, E, k, dt) != MOE_OK || check_options(opt, T, dt) != MOE_OK) return 0;
   return carve_ext_workspace(nullptr, T, d, ffn, E, k, dt, opt->norm_weight != nullptr,
                              opt->n_shared, opt->shared_ffn)
       .bytes;
@@ -247,7 +257,7 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
                            size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_layer(T, d, ffn, E, k, dt);
   if (st != MOE_OK) return st;
-  st = check_options(opt, T);
+  st = check_options(opt, T, dt);
   if (st != MOE_OK) return st;
   if (!ok_dtype(out_dt)) return MOE_UNSUPPORTED;
   if (T == 0) return MOE_OK;

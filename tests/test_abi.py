@@ -75,6 +75,7 @@ def test_forward_validation(L):
         return L.moe_forward(p, p, p, p, p, None, a["T"], a["d"], a["ffn"], a["E"], a["k"],
                              a["dt"], p, a["odt"], None, None, None, p, ws_bytes, None)
 
+    assert call(T=1 << 20, d=4096) == UNSUPPORTED          # T*d*2 bytes reach 2^32
     assert call(k=0) == INVALID
     assert call(k=5) == INVALID
     assert call(d=0) == INVALID
