@@ -140,10 +140,11 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
 
   // Each wave takes U consecutive 32-wide slices at a time and issues all
   // their loads before the first product, so a wave waits for one memory
-  // round trip per U slices (this kernel is latency-bound for small T).
+  // round trip per U slices (this kernel is latency-bound for small T):
+  // with 16 waves and U = 8 a width of 4096 takes one round trip.
   // Out-of-range rows, experts and columns load from a valid address and
   // are replaced by zeros, which keeps the loads unconditional.
-  constexpr int U = 4;
+  constexpr int U = NB <= 2 ? 8 : 4;  // registers: U * (1 + NB) 16-byte operands
   const int nk = (d + 31) / 32;
   const uint4 zero = make_uint4(0, 0, 0, 0);
   for (int kc0 = wave * U; kc0 < nk; kc0 += NW * U) {
