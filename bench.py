@@ -182,9 +182,11 @@ def main():
     gu_flops = 4.0 * rows * w.d * w.ffn
     gu_bytes = touched * 2 * w.ffn * w.d * 2 + rows * w.d * 2 + rows * w.ffn * 2
     gu_s = stage_ms["gate_up"] / 1e3
-    if rows > 32 * w.E:   # tiled MFMA kernels (the library's own switch)
+    if rows > 32 * w.E:   # tiled MFMA kernels (the library's own switches)
         kern = "expert_gemm_bf16_kernel"
-        roof = {"kernel": "expert_gemm_bf16_kernel<true, 8>", "bound": "mfma",
+        kname = ("expert_gemm_tall_kernel<true>" if rows >= 2 * 384 * w.E
+                 else "expert_gemm_bf16_kernel<true, 8>")
+        roof = {"kernel": kname, "bound": "mfma",
                 "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:                   # weight-streaming kernels
         kern = "expert_stream_kernel"

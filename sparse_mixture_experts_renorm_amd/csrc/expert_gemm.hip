@@ -10,7 +10,9 @@
 // because rounding y to bf16 as well would spend about half of the 2e-2 x RMS
 // error budget of bf16 workloads on top of h's rounding.
 //
-// bf16 path (gfx950). One workgroup of 8 waves per CU (two per SIMD)
+// bf16 path (gfx950), two tile shapes: 256 x 256 (below) and the tall
+// 384 x 256 tiles further down, taken when the experts average at least 768
+// rows. One workgroup of 8 waves per CU (two per SIMD)
 // computes a 256 x 256 tile: 256 permuted rows against 256 weight rows
 // (gate/up: 128 gate rows and the same 128 up rows, giving 128 columns of h;
 // down: 256 columns of y). Each wave owns a 128 x 64 part: 8 accumulators of
@@ -62,10 +64,10 @@ struct Tile {
 // rounds on n_cu CUs, counted in units of a whole tile, with at least
 // kMinSplitSteps of the nk reduction steps in every part (shorter parts
 // would spend more on the extra partial sums than they save).
+// s_tile: six ints of LDS for broadcasting the result from thread 0.
 template <int BM>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
-                         int n_cu, int nk, Tile* out) {
-  __shared__ int s_tile[6];
+                         int n_cu, int nk, Tile* out, int* s_tile) {
   if (threadIdx.x == 0) {
     int base = 0;
     for (int e = 0; e < E; ++e) {
@@ -168,7 +170,8 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
   const int nk = (K + TK - 1) / TK;
-  const bool have = map_tile<TM>(offsets, E, nN, max_split, n_cu, nk, &tile);
+  __shared__ int s_tile[6];
+  const bool have = map_tile<TM>(offsets, E, nN, max_split, n_cu, nk, &tile, s_tile);
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;
   // reduction steps [kbeg, kend) of this tile
@@ -358,6 +361,183 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   }
 }
 
+// Tall tiles: 384 permuted rows x 256 weight rows, 8 waves (two per SIMD) of
+// 96 x 128 (3 x 4 accumulators of v_mfma_f32_32x32x16_bf16, 192 fp32 per
+// lane), two 80 KB LDS stages (the whole LDS). Each step moves 80 KB into the
+// CU for 12.6 MFLOP, 17% fewer bytes per FLOP than the 256 x 256 tile; the
+// cost is coarser row padding, so the host takes these tiles only when the
+// experts average at least two tiles' worth of rows. Same loads, swizzle,
+// stages and epilogue as the 256 x 256 kernel; which operand and which
+// weight matrix each load instruction serves is fixed per unrolled index, so
+// the compiler keeps the choice in scalar code (chosen at run time, the
+// pointer selection went through scratch memory).
+constexpr int TM3 = 384;              // permuted rows per tile
+constexpr int STAGE_A3 = TM3 * TK * 2;  // 48 KB
+constexpr int NW3 = 8;
+constexpr int NINS = (TM3 + TW) / 8;  // 1 KB load instructions per stage (80)
+constexpr int IPW3 = NINS / NW3;      // 10
+constexpr int MBW = 3, NBW3 = 4;      // 32-row blocks per wave: tokens, weights
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(NW3 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
+                             const int32_t* __restrict__ offsets, int E,
+                             const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
+                             int K, void* __restrict__ Cv, int max_split, int n_cu,
+                             size_t c_split, int32_t* __restrict__ split_out) {
+  __shared__ __attribute__((aligned(1024))) char lds0a[STAGE_A3];
+  __shared__ __attribute__((aligned(1024))) char lds0b[STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1a[STAGE_A3];
+  __shared__ __attribute__((aligned(1024))) char lds1b[STAGE];
+  auto buf = [&](int st, int op) -> char* {
+    return st == 0 ? (op ? lds0b : lds0a) : (op ? lds1b : lds1a);
+  };
+  const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
+  Tile tile;
+  const int nk = (K + TK - 1) / TK;
+  const bool have = map_tile<TM3>(offsets, E, nN, max_split, n_cu, nk, &tile,
+                                  reinterpret_cast<int*>(lds1a));
+  __syncthreads();
+  if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
+  if (!have) return;
+  const int kbeg = tile.ks * nk / tile.S, kend = (tile.ks + 1) * nk / tile.S;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // instruction q = wave + 8 j: q < 48 loads A rows 8q .. 8q+7, else B rows
+  // 8(q-48) ..; lane l writes row r of its operand, slot l%8, which holds
+  // chunk (l%8) ^ ((r >> 1) & 7)
+  const int n0 = GATE_UP ? tile.nt * 128 : tile.nt * TW;
+  const char* a_base = reinterpret_cast<const char*>(A);
+  const size_t wexp = static_cast<size_t>(tile.e) * N * K * 2;
+  const char* g_base = reinterpret_cast<const char*>(B0) + wexp;
+  const char* u_base = reinterpret_cast<const char*>(GATE_UP ? B1 : B0) + wexp;
+  // instruction q = wave + 8 j: j < 6 are A instructions (q < 48: A rows
+  // 8q .. 8q+7), j >= 6 B instructions (B rows 8(wave + 8(j-6)) ..; for
+  // gate/up j = 6, 7 are gate rows and j = 8, 9 the same rows of up). Lane l
+  // writes row r = 8*qq + l/8, slot l%8, holding chunk (l%8) ^ ((r >> 1) & 7);
+  // (r >> 1) & 7 = (4*qq + l/16) & 7 = (4*wave + l/16) & 7 for every j.
+  constexpr int JA = TM3 / 8 / NW3;  // 6
+  const int ch = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  uint32_t src_off[IPW3];
+#pragma unroll
+  for (int j = 0; j < IPW3; ++j) {
+    const bool isA = j < JA;
+    const int qq = isA ? wave + NW3 * j : wave + NW3 * (j - JA);
+    const int r = qq * 8 + (lane >> 3);
+    uint32_t row;
+    if (isA) {
+      const int rr = r < tile.rows ? r : r % tile.rows;
+      row = GATE_UP ? static_cast<uint32_t>(sorted_token[tile.row0 + rr])
+                    : static_cast<uint32_t>(tile.row0 + rr);
+    } else {
+      row = static_cast<uint32_t>(min(n0 + (GATE_UP ? (r & 127) : r), N - 1));
+    }
+    src_off[j] = row * static_cast<uint32_t>(K) * 2u + ch * 16u;
+  }
+  const char* zero = reinterpret_cast<const char*>(g_zero_page);
+  auto issue = [&](int kt, int st) {
+    const int k0 = kt * TK;
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+    const bool kin = k0 + ch * 8 < K;
+#pragma unroll
+    for (int j = 0; j < IPW3; ++j) {
+      const bool isA = j < JA;
+      const int qq = isA ? wave + NW3 * j : wave + NW3 * (j - JA);
+      const char* base = isA ? a_base : ((GATE_UP && j >= JA + 2) ? u_base : g_base);
+      load_lds16(kin ? base + (src_off[j] + kb) : zero, buf(st, isA ? 0 : 1) + qq * 1024);
+    }
+  };
+  const int xr = ((lane & 31) >> 1) & 7, half = lane >> 5;
+  int fa_off[MBW], fb_off[NBW3];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) fa_off[i] = (wm * 96 + i * 32 + (lane & 31)) * 128;
+#pragma unroll
+  for (int i = 0; i < NBW3; ++i) {
+    // gate/up: blocks 0,1 gate rows wn*64 + 32i, blocks 2,3 the same rows of up
+    const int brow = GATE_UP ? (i >> 1) * 128 + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+    fb_off[i] = (brow + (lane & 31)) * 128;
+  }
+  f32x16 acc[NBW3][MBW];
+#pragma unroll
+  for (int a = 0; a < NBW3; ++a)
+#pragma unroll
+    for (int b = 0; b < MBW; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  auto step = [&](int kt, int st, bool next) {
+    if (next) issue(kt + 1, st ^ 1);
+#pragma unroll
+    for (int s = 0; s < TK / 16; ++s) {
+      const int slot = ((2 * s + half) ^ xr) << 4;
+      bf16x8 fa[MBW];
+#pragma unroll
+      for (int i = 0; i < MBW; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(buf(st, 0) + fa_off[i] + slot);
+#pragma unroll
+      for (int nb = 0; nb < NBW3; ++nb) {
+        const bf16x8 fb = *reinterpret_cast<const bf16x8*>(buf(st, 1) + fb_off[nb] + slot);
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa[mb], acc[nb][mb], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nsteps = kend - kbeg;
+  if (nsteps > 0) issue(kbeg, 0);
+  for (int p = 0; p + 1 < nsteps; p += 2) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int kt = kbeg + p + r;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      step(kt, r, kt + 1 < kend);
+    }
+  }
+  if (nsteps & 1) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    step(kend - 1, 0, false);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int m = wm * 96 + mb * 32 + (lane & 31);
+    if (m >= tile.rows) continue;
+    const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nloc = 8 * g + 4 * half;
+      if (GATE_UP) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int n = tile.nt * 128 + wn * 64 + nb * 32 + nloc;
+          if (n < N) {
+            float hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + 2][mb][4 * g + i];
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
+                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NBW3; ++nb) {
+          const int n = tile.nt * TW + wn * 128 + nb * 32 + nloc;
+          if (n < N)
+            *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
+                make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                            acc[nb][mb][4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 path: one thread per output element, plain fp32 FMA loops. Only for
 // the fp32 dtype (small parity workloads); grid = (rows, column blocks).
@@ -411,6 +591,10 @@ unsigned tile_grid(int rows, int E, int BM, int nN, int splits) {
   return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds);
 }
 
+// Tall tiles pay off once the experts average two tiles' worth of rows
+// (their padding is then at most a third of a tile over two or more).
+bool use_tall_tiles(int rows, int E) { return rows >= 2 * TM3 * E; }
+
 int cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -433,6 +617,12 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
   }
   if (use_stream_path(rows, E))
     return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows, h, s);
+  if (use_tall_tiles(rows, E)) {
+    expert_gemm_tall_kernel<true><<<tile_grid(rows, E, TM3, (ffn + 127) / 128, 1), NW3 * 64, 0, s>>>(
+        static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
+        static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
+    return launch_status();
+  }
   expert_gemm_bf16_kernel<true, kWaves><<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), kWaves * 64, 0, s>>>(
       static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
       static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
@@ -450,6 +640,13 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
     return launch_status();
   }
   if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, rows, y, split, s);
+  if (use_tall_tiles(rows, E)) {
+    expert_gemm_tall_kernel<false><<<tile_grid(rows, E, TM3, (d + TW - 1) / TW, kMaxDownSplit),
+                                     NW3 * 64, 0, s>>>(
+        static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
+        nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
+    return launch_status();
+  }
   expert_gemm_bf16_kernel<false, kWaves><<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64,
                                    0, s>>>(
       static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),

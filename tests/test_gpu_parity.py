@@ -116,6 +116,11 @@ EXPERT_SHAPES = [
     (60, 128, 192, 4, 2, "bf16", "all_same"),    # 60 rows on experts 0 and 1 (two row blocks)
     (16, 64, 96, 8, 1, "bf16", "one_heavy"),     # k = 1, every token on expert 7
     (32, 4096, 14336, 8, 2, "bf16", "random"),   # decode shape
+    # at least 768 rows per expert on average: the tall-tile kernels
+    (3200, 256, 320, 4, 1, "bf16", "random"),
+    (1600, 272, 336, 2, 2, "bf16", "random"),    # ragged K and N tails on both passes
+    (1700, 128, 192, 3, 3, "bf16", "one_heavy"),  # k = E
+    (2000, 128, 256, 4, 2, "bf16", "all_same"),  # 2000 rows on experts 0 and 1, the rest empty
 ]
 
 
