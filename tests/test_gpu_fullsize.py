@@ -64,3 +64,39 @@ def test_fullsize_sampled_parity(M, name):
                        inp["w_down"], w.k, inp["router_bias"], 2e-2, tokens=tok)
     say(f"full-size {name}: max err {st['max_rel_err']:.3e} x RMS (bar 2e-2), "
         f"sample near-ties {st['near_ties']}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_fullsize_block_options(M, name):
+    """The extended forward in the configuration the benchmark's extras time
+    (capacity factor 1.25, RMSNorm, residual, one shared expert as wide as
+    the routed ones), on sampled tokens. At this balance no expert reaches
+    its capacity, which the test asserts, so every token's output depends on
+    its own routing only and near-tie tokens may take any valid routing."""
+    import test_gpu_ext as X
+    w = wl.WORKLOADS[name]
+    say(f"full-size block options {name}: generating inputs")
+    inp = wl.make_layer_inputs(w, seed=0)
+    ext = wl.make_block_extras(w.d, 1, w.ffn, w.dtype, seed=0)
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    shared = (dev_tensor(ext["s_gate"]), dev_tensor(ext["s_up"]), dev_tensor(ext["s_down"]))
+    say(f"full-size block options {name}: moe_forward_ext")
+    out, ex = M.moe_forward_ext(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"],
+                                w.k, router_bias=dv["router_bias"], capacity_factor=1.25,
+                                norm_weight=dev_tensor(ext["norm_weight"]), residual=True,
+                                shared=shared, want_counts=True, want_routed_counts=True)
+    torch.cuda.synchronize()
+    got = host(out)
+    kept, routed = host(ex["counts"]), host(ex["routed_counts"])
+    cap = O.capacity(w.T, w.E, w.k, 1.25)
+    assert routed.max() <= cap and np.array_equal(kept, routed), "an expert reached its capacity"
+    rng = np.random.default_rng(99)
+    tok = np.sort(rng.choice(w.T, size=min(SAMPLE[name], w.T), replace=False))
+    say(f"full-size block options {name}: oracle on {len(tok)} tokens")
+    sub = dict(inp, x=inp["x"][tok])
+    ref, _ = O.moe_forward(sub["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                           w.k, inp["router_bias"], norm_weight=ext["norm_weight"],
+                           residual=True, shared=(ext["s_gate"], ext["s_up"], ext["s_down"]))
+    worst, amb = X._compare(got[tok], ref, None, sub, ext, w.k, 0.0, True, True, 1, True)
+    say(f"full-size block options {name}: worst {worst:.3e} x RMS, near-ties {amb}")
