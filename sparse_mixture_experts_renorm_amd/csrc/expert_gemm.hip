@@ -366,11 +366,14 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 // lane), two 80 KB LDS stages (the whole LDS). Each step moves 80 KB into the
 // CU for 12.6 MFLOP, 17% fewer bytes per FLOP than the 256 x 256 tile; the
 // cost is coarser row padding, so the host takes these tiles only when the
-// experts average at least two tiles' worth of rows. Same loads, swizzle,
-// stages and epilogue as the 256 x 256 kernel; which operand and which
-// weight matrix each load instruction serves is fixed per unrolled index, so
-// the compiler keeps the choice in scalar code (chosen at run time, the
-// pointer selection went through scratch memory).
+// experts average at least two tiles' worth of rows. Same swizzle, stages
+// and epilogue as the 256 x 256 kernel, but the next step's loads are spread
+// over the first half of each step (see step below). Which operand and
+// which weight matrix each load instruction serves is fixed per unrolled
+// index, so the compiler keeps the choice in scalar code (chosen at run
+// time, the pointer selection went through scratch memory). KMASK: the
+// reduction length is not a multiple of the step, so chunks past it read
+// the zero page.
 constexpr int TM3 = 384;              // permuted rows per tile
 constexpr int STAGE_A3 = TM3 * TK * 2;  // 48 KB
 constexpr int NW3 = 8;
@@ -378,7 +381,7 @@ constexpr int NINS = (TM3 + TW) / 8;  // 1 KB load instructions per stage (80)
 constexpr int IPW3 = NINS / NW3;      // 10
 constexpr int MBW = 3, NBW3 = 4;      // 32-row blocks per wave: tokens, weights
 
-template <bool GATE_UP>
+template <bool GATE_UP, bool KMASK>
 __global__ __launch_bounds__(NW3 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
                              const int32_t* __restrict__ offsets, int E,
@@ -468,21 +471,60 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  auto step = [&](int kt, int st, bool next) {
-    if (next) issue(kt + 1, st ^ 1);
+  // Load instruction j of step kt into stage st. Without KMASK every chunk
+  // of a step lies inside K: one uniform base plus the lane's 32-bit offset.
+  auto issue_j = [&](int kt, int st, int j) __attribute__((always_inline)) {
+    const int k0 = kt * TK;
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+    const bool isA = j < JA;
+    const int qq = isA ? wave + NW3 * j : wave + NW3 * (j - JA);
+    const char* base = isA ? a_base : ((GATE_UP && j >= JA + 2) ? u_base : g_base);
+    char* dst = buf(st, isA ? 0 : 1) + qq * 1024;
+    if constexpr (KMASK) {
+      load_lds16(k0 + ch * 8 < K ? base + (src_off[j] + kb) : zero, dst);
+    } else {
+      load_lds16((base + kb) + src_off[j], dst);
+    }
+  };
+  // One step on stage st: 16 groups of one weight fragment times the three
+  // token fragments (3 MFMAs). The fragments of group g+1 are read before the
+  // MFMAs of group g, and the first kLoadGroups groups each issue a share of
+  // the next step's loads, so the load instructions go out at the rate the
+  // address unit takes them instead of stalling every wave at the start of
+  // the step; the scheduling fences keep that order. In the last step the
+  // loads re-read an in-range step into the idle stage, which keeps the
+  // instruction stream free of branches.
+  constexpr int kGroups = (TK / 16) * NBW3;  // 16
+  constexpr int kLoadGroups = 8;
+  auto step = [&](int kt, int st) __attribute__((always_inline)) {
+    const int kload = min(kt + 1, nk - 1);
+    auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
+    };
+    bf16x8 fa[2][MBW], fb[2];
 #pragma unroll
-    for (int s = 0; s < TK / 16; ++s) {
-      const int slot = ((2 * s + half) ^ xr) << 4;
-      bf16x8 fa[MBW];
+    for (int i = 0; i < MBW; ++i) fa[0][i] = rd(0, fa_off[i], 0);
+    fb[0] = rd(1, fb_off[0], 0);
 #pragma unroll
-      for (int i = 0; i < MBW; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(buf(st, 0) + fa_off[i] + slot);
+    for (int g = 0; g < kGroups; ++g) {
+      const int s = g / NBW3, nb = g % NBW3, ca = s & 1, cb = g & 1;
+      if (g + 1 < kGroups) {
+        const int s1 = (g + 1) / NBW3, nb1 = (g + 1) % NBW3;
+        if (nb1 == 0) {
 #pragma unroll
-      for (int nb = 0; nb < NBW3; ++nb) {
-        const bf16x8 fb = *reinterpret_cast<const bf16x8*>(buf(st, 1) + fb_off[nb] + slot);
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa[mb], acc[nb][mb], 0, 0, 0);
+          for (int i = 0; i < MBW; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
+        }
+        fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
       }
+      if (g < kLoadGroups) {
+#pragma unroll
+        for (int j = g * IPW3 / kLoadGroups; j < (g + 1) * IPW3 / kLoadGroups; ++j)
+          issue_j(kload, st ^ 1, j);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -491,16 +533,15 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   for (int p = 0; p + 1 < nsteps; p += 2) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int kt = kbeg + p + r;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      step(kt, r, kt + 1 < kend);
+      step(kbeg + p + r, r);
     }
   }
   if (nsteps & 1) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    step(kend - 1, 0, false);
+    step(kend - 1, 0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -618,7 +659,8 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
   if (use_stream_path(rows, E))
     return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows, h, s);
   if (use_tall_tiles(rows, E)) {
-    expert_gemm_tall_kernel<true><<<tile_grid(rows, E, TM3, (ffn + 127) / 128, 1), NW3 * 64, 0, s>>>(
+    auto kern = d % TK ? expert_gemm_tall_kernel<true, true> : expert_gemm_tall_kernel<true, false>;
+    kern<<<tile_grid(rows, E, TM3, (ffn + 127) / 128, 1), NW3 * 64, 0, s>>>(
         static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
         static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
     return launch_status();
@@ -641,8 +683,8 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
   }
   if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, rows, y, split, s);
   if (use_tall_tiles(rows, E)) {
-    expert_gemm_tall_kernel<false><<<tile_grid(rows, E, TM3, (d + TW - 1) / TW, kMaxDownSplit),
-                                     NW3 * 64, 0, s>>>(
+    auto kern = ffn % TK ? expert_gemm_tall_kernel<false, true> : expert_gemm_tall_kernel<false, false>;
+    kern<<<tile_grid(rows, E, TM3, (d + TW - 1) / TW, kMaxDownSplit), NW3 * 64, 0, s>>>(
         static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
         nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
     return launch_status();
