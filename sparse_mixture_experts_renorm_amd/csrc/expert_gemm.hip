@@ -148,7 +148,7 @@ constexpr int STAGE = TM * TK * 2;  // bytes per operand and stage (32 KB)
 // NW waves per workgroup: 4 (wave tile 128 x 128, one wave per SIMD) or 8
 // (wave tile 128 x 64, two waves per SIMD, so one wave's MFMAs run while the
 // other waits to issue its loads).
-template <bool GATE_UP, int NW>
+template <bool GATE_UP, int NW, bool KMASK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
                              const int32_t* __restrict__ offsets, int E,
@@ -221,16 +221,19 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
     b_base[j] = reinterpret_cast<const char*>((GATE_UP && r >= 128) ? B1 : B0) + wexp;
   }
   const char* zero = reinterpret_cast<const char*>(g_zero_page);
-  // load instruction j (0 .. 2*IPW-1: A then B) of step kt into stage st
-  auto issue_one = [&](int kt, int st, int j) {
+  // load instruction j (0 .. 2*IPW-1: A then B) of step kt into stage st;
+  // without KMASK every chunk of the step lies inside K
+  auto issue_one = [&](int kt, int st, int j) __attribute__((always_inline)) {
     const int k0 = kt * TK;
     const int jj = j % IPW;
-    const bool kin = k0 + kchunk[jj] * 8 < K;
     const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
-    if (j < IPW)
-      load_lds16(kin ? a_base + (a_off[jj] + kb) : zero, buf(st, 0) + (wave * IPW + jj) * 1024);
+    const char* base = j < IPW ? a_base : b_base[jj];
+    const uint32_t off = j < IPW ? a_off[jj] : b_off[jj];
+    char* dst = buf(st, j < IPW ? 0 : 1) + (wave * IPW + jj) * 1024;
+    if constexpr (KMASK)
+      load_lds16(k0 + kchunk[jj] * 8 < K ? base + (off + kb) : zero, dst);
     else
-      load_lds16(kin ? b_base[jj] + (b_off[jj] + kb) : zero, buf(st, 1) + (wave * IPW + jj) * 1024);
+      load_lds16((base + kb) + off, dst);
   };
   // ---- fragment reads: row R's chunk c is at R*128 + ((c ^ ((R >> 1) & 7)) << 4);
   // every row this lane reads has R % 32 == lane % 32.
@@ -255,45 +258,45 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  auto read_frags = [&](int st, int s, bf16x8* fa, bf16x8* fb) {
-    const int slot = ((2 * s + half) ^ xr) << 4;
+  // One step on stage st: groups of one weight fragment times the four token
+  // fragments (4 MFMAs). The fragments of group g+1 are read before the MFMAs
+  // of group g, and the first half of the groups each issue a share of the
+  // next step's loads, so the load instructions go out at the rate the
+  // address unit takes them instead of stalling every wave at the start of
+  // the step; the scheduling fences keep that order. In the last step the
+  // loads re-read an in-range step into the idle stage, which keeps the
+  // instruction stream free of branches.
+  constexpr int kGroups = (TK / 16) * NBW;
+  constexpr int kLoadGroups = kGroups / 2;
+  auto step = [&](int kt, int st) __attribute__((always_inline)) {
+    const int kload = min(kt + 1, nk - 1);
+    auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
+    };
+    bf16x8 fa[2][4], fb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(buf(st, 0) + fa_off[i] + slot);
+    for (int i = 0; i < 4; ++i) fa[0][i] = rd(0, fa_off[i], 0);
+    fb[0] = rd(1, fb_off[0], 0);
 #pragma unroll
-    for (int i = 0; i < NBW; ++i) fb[i] = *reinterpret_cast<const bf16x8*>(buf(st, 1) + fb_off[i] + slot);
-  };
-  auto mma16 = [&](const bf16x8* fa, const bf16x8* fb) {
+    for (int g = 0; g < kGroups; ++g) {
+      const int s = g / NBW, nb = g % NBW, ca = s & 1, cb = g & 1;
+      if (g + 1 < kGroups) {
+        const int s1 = (g + 1) / NBW, nb1 = (g + 1) % NBW;
+        if (nb1 == 0) {
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
+          for (int i = 0; i < 4; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
+        }
+        fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
+      }
+      if (g < kLoadGroups) {
+#pragma unroll
+        for (int j = g * 2 * IPW / kLoadGroups; j < (g + 1) * 2 * IPW / kLoadGroups; ++j)
+          issue_one(kload, st ^ 1, j);
+      }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
-  };
-  // One step on stage st: the next step's loads go out first, as one burst
-  // (a load that waits for a free slot in the memory pipeline then delays
-  // the MFMAs once per step, not between every few MFMAs); then, while the
-  // 16 MFMAs of substep s run, the fragment reads of substep s+1 are issued.
-  auto step = [&](int kt, int st, bool next) {
-    if (next) {
-#pragma unroll
-      for (int j = 0; j < 2 * IPW; ++j) issue_one(kt + 1, st ^ 1, j);
-    }
-    bf16x8 fa[2][4], fb[2][NBW];
-    read_frags(st, 0, fa[0], fb[0]);
-#pragma unroll
-    for (int s = 0; s < TK / 16; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < TK / 16) read_frags(st, s + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      mma16(fa[cur], fb[cur]);
-      if (s + 1 < TK / 16) {
-        // one fragment read after each of the first 4 + NBW MFMAs
-#pragma unroll
-        for (int i = 0; i < 4 + NBW; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 fragment read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBW - 4 - NBW, 0);
-      }
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -301,25 +304,30 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // waits for its own); the barrier then makes every wave's loads visible
   // and guarantees that the other stage, overwritten during step kt, is no
   // longer read. Steps go in pairs (stage 0, stage 1); an odd last step runs
-  // on stage 0 and issues nothing.
+  // on stage 0.
   const int nsteps = kend - kbeg;
   if (nsteps > 0) {
+    const int k0 = kbeg * TK;
 #pragma unroll
-    for (int j = 0; j < 2 * IPW; ++j) issue_one(kbeg, 0, j);
+    for (int j = 0; j < 2 * IPW; ++j) {
+      const int jj = j % IPW;
+      const bool kin = k0 + kchunk[jj] * 8 < K;
+      const char* src = j < IPW ? a_base + (a_off[jj] + k0 * 2u) : b_base[jj] + (b_off[jj] + k0 * 2u);
+      load_lds16(kin ? src : zero, buf(0, j < IPW ? 0 : 1) + (wave * IPW + jj) * 1024);
+    }
   }
   for (int p = 0; p + 1 < nsteps; p += 2) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int kt = kbeg + p + r;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      step(kt, r, kt + 1 < kend);
+      step(kbeg + p + r, r);
     }
   }
   if (nsteps & 1) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    step(kend - 1, 0, false);
+    step(kend - 1, 0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -665,7 +673,8 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
         static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
     return launch_status();
   }
-  expert_gemm_bf16_kernel<true, kWaves><<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), kWaves * 64, 0, s>>>(
+  auto kern = d % TK ? expert_gemm_bf16_kernel<true, kWaves, true> : expert_gemm_bf16_kernel<true, kWaves, false>;
+  kern<<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), kWaves * 64, 0, s>>>(
       static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
       static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
   return launch_status();
@@ -689,8 +698,8 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
         nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
     return launch_status();
   }
-  expert_gemm_bf16_kernel<false, kWaves><<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64,
-                                   0, s>>>(
+  auto kern = ffn % TK ? expert_gemm_bf16_kernel<false, kWaves, true> : expert_gemm_bf16_kernel<false, kWaves, false>;
+  kern<<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64, 0, s>>>(
       static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
       nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
   return launch_status();
