@@ -184,8 +184,9 @@ def main():
     gu_s = stage_ms["gate_up"] / 1e3
     if rows > 32 * w.E:   # tiled MFMA kernels (the library's own switches)
         kern = "expert_gemm_bf16_kernel"
-        kname = ("expert_gemm_tall_kernel<true>" if rows >= 2 * 384 * w.E
-                 else "expert_gemm_bf16_kernel<true, 8>")
+        kmask = "true" if w.d % 64 else "false"
+        kname = (f"expert_gemm_tall_kernel<true, {kmask}>" if rows >= 2 * 384 * w.E
+                 else f"expert_gemm_bf16_kernel<true, 8, {kmask}>")
         roof = {"kernel": kname, "bound": "mfma",
                 "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:                   # weight-streaming kernels
