@@ -91,8 +91,9 @@ def log(msg):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clock takes a few tens of milliseconds of load to settle
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill",
                     choices=["tiny", "small", "prefill", "decode", "skewed"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
