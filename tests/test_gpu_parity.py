@@ -121,6 +121,10 @@ EXPERT_SHAPES = [
     (1600, 272, 336, 2, 2, "bf16", "random"),    # ragged K and N tails on both passes
     (1700, 128, 192, 3, 3, "bf16", "one_heavy"),  # k = E
     (2000, 128, 256, 4, 2, "bf16", "all_same"),  # 2000 rows on experts 0 and 1, the rest empty
+    # long reductions with a tail (6160 = 96 * 64 + 16): the down pass splits its
+    # reduction and the last step of each part reads past K
+    (1600, 256, 6160, 2, 1, "bf16", "random"),   # tall tiles
+    (600, 128, 6160, 2, 1, "bf16", "random"),    # 256 x 256 tiles
 ]
 
 
