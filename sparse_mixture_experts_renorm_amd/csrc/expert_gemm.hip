@@ -18,13 +18,15 @@
 // down: 256 columns of y). Each wave owns a 128 x 64 part: 8 accumulators of
 // v_mfma_f32_32x32x16_bf16 (128 fp32 per lane), so each 16-byte fragment read
 // from LDS feeds 2 or 4 MFMAs; with two waves per SIMD one wave's MFMAs run
-// while the other waits to issue its loads. The reduction dimension moves
-// in steps of 64 through two LDS stages (64 KB each): the loads of step s+1
-// are issued with global_load_lds_dwordx4 (memory to LDS without VGPRs) just
-// before the MFMAs of step s. Each lane supplies its own address, which is
-// how the token gather of the gate/up pass is done; lanes past K read a
-// 16-byte zero page. The step time is set by the bytes each CU must move
-// from L2 per step (64 KB per 8.4 MFLOP), not by the LDS or the MFMAs.
+// while the other waits for its data. The reduction dimension moves in
+// steps of 64 through two LDS stages (64 KB each): the loads of step s+1 go
+// from memory straight to LDS (buffer_load_dwordx4 ... lds, no VGPRs) while
+// the MFMAs of step s run, spread over the first half of the step. Each lane
+// supplies its own 32-bit offset, which is how the token gather of the
+// gate/up pass is done; when K is not a multiple of 64, global loads whose
+// lanes past K read a 16-byte zero page are used instead. The step waits
+// mostly on the latency of the L2 and the data it returns, not on the LDS
+// or the MFMAs.
 // LDS rows are 128 bytes (64 bf16); chunk c (16 bytes) of row r is stored at
 // slot c ^ ((r >> 1) & 7). gfx950 serves a 16-byte-per-lane LDS read 16 lanes
 // at a time over 64 four-byte banks; a fragment read sends 16 consecutive
