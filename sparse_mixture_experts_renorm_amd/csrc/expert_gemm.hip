@@ -204,7 +204,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // which holds chunk (l%8) ^ ((r >> 1) & 7).
   // Sources are 32-bit byte offsets from one base per operand. Rows past the
   // tile's valid rows (or past N) repeat valid rows: their products are
-  // computed but never stored. Chunks past K read the zero page.
+  // computed but never stored. With KMASK, chunks past K read the zero page.
   // Tile row r of the weight operand: gate/up rows 0-127 are gate rows
   // n0 .. n0+127, rows 128-255 the same rows of up; down rows are n0 + r.
   const int n0 = GATE_UP ? tile.nt * 128 : tile.nt * TW;
@@ -434,9 +434,6 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // instruction q = wave + 8 j: q < 48 loads A rows 8q .. 8q+7, else B rows
-  // 8(q-48) ..; lane l writes row r of its operand, slot l%8, which holds
-  // chunk (l%8) ^ ((r >> 1) & 7)
   const int n0 = GATE_UP ? tile.nt * 128 : tile.nt * TW;
   const char* a_base = reinterpret_cast<const char*>(A);
   const size_t wexp = static_cast<size_t>(tile.e) * N * K * 2;
