@@ -199,9 +199,9 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- direct-load sources. Per stage each operand is 256 rows x 128 bytes,
-  // loaded by 1 KB instructions of 8 rows; wave w issues instructions
-  // 8w .. 8w+7. In instruction q lane l writes row r = q*8 + l/8, slot l%8,
-  // which holds chunk (l%8) ^ ((r >> 1) & 7).
+  // loaded by 32 instructions of 1 KB (8 rows); wave w issues instructions
+  // IPW*w .. IPW*w + IPW-1 of each operand. In instruction q lane l writes
+  // row r = q*8 + l/8, slot l%8, which holds chunk (l%8) ^ ((r >> 1) & 7).
   // Sources are 32-bit byte offsets from one base per operand. Rows past the
   // tile's valid rows (or past N) repeat valid rows: their products are
   // computed but never stored. With KMASK, chunks past K read the zero page.
