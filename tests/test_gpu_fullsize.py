@@ -100,3 +100,33 @@ def test_fullsize_block_options(M, name):
                            residual=True, shared=(ext["s_gate"], ext["s_up"], ext["s_down"]))
     worst, amb = X._compare(got[tok], ref, None, sub, ext, w.k, 0.0, True, True, 1, True)
     say(f"full-size block options {name}: worst {worst:.3e} x RMS, near-ties {amb}")
+
+
+@pytest.mark.timeout(900)
+def test_largest_batch_byte_offsets(M):
+    """The largest batch the ABI accepts at the prefill widths: T*k*ffn*2 bytes
+    of h just under 2^32 (T = 74898, 4.29e9 bytes), so the down pass's 32-bit
+    byte offsets into h reach the top of their range. The sample holds the
+    last tokens of the last expert by the oracle's own routing (the highest
+    permuted rows, hence the highest offsets) and a few random ones."""
+    T, d, ffn, E, k = 74898, 4096, 14336, 8, 2
+    assert T * k * ffn * 2 < 2 ** 32 <= (T + 1) * k * ffn * 2
+    say(f"largest batch T={T}: generating inputs")
+    inp = wl.make_custom_inputs(T, d, ffn, E, "bf16", seed=0)
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    say("largest batch: moe_forward")
+    out = M.moe_forward(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], k)
+    torch.cuda.synchronize()
+    got = host(out)
+    del dv, out
+    torch.cuda.empty_cache()
+    say("largest batch: oracle routing of every token")
+    L = O.router_logits(inp["x"], inp["w_router"], None)
+    _, idx, _ = O.route(L, k)
+    last = np.flatnonzero((idx == E - 1).any(axis=1))[-8:]
+    rng = np.random.default_rng(7)
+    tok = np.unique(np.concatenate([last, rng.choice(T, size=8, replace=False)]))
+    say(f"largest batch: oracle on {len(tok)} tokens")
+    st = compare_layer(got[tok], inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                       inp["w_down"], k, None, 2e-2, tokens=tok)
+    say(f"largest batch: max err {st['max_rel_err']:.3e} x RMS, near-ties {st['near_ties']}")
