@@ -48,6 +48,8 @@
 // rounds instead, the L2 fetched a third more).
 #include "common.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -57,6 +59,7 @@ constexpr int kMinSplitSteps = 48;
 struct Tile {
   int e, row0, rows, nt;
   int ks, S;  // split of the reduction dimension: this tile computes part ks of S
+  int half;   // -1: the whole column tile; 0 or 1: that half of its weight rows
 };
 
 // Map this workgroup to a tile of BM rows; returns false if it has none.
@@ -66,8 +69,13 @@ struct Tile {
 // rounds on n_cu CUs, counted in units of a whole tile, with at least
 // kMinSplitSteps of the nk reduction steps in every part (shorter parts
 // would spend more on the extra partial sums than they save).
-// s_tile: six ints of LDS for broadcasting the result from thread 0.
-template <int BM>
+// With TAIL, an XCD whose tile count leaves a last round at most half full
+// (r tiles for its n_cu/8 CUs, 2r <= n_cu/8) runs those r tiles as 2r
+// half-width tiles, so its last round takes about half a tile's time
+// instead of a whole one (the workgroups of the halves come last in the
+// XCD's order); the grid provides n_cu/16 extra slots per XCD for them.
+// s_tile: seven ints of LDS for broadcasting the result from thread 0.
+template <int BM, bool TAIL = false>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
                          int n_cu, int nk, Tile* out, int* s_tile) {
   if (threadIdx.x == 0) {
@@ -87,9 +95,23 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int
     const int total = base * S;
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    int L = xcd * per_xcd + slot;
+    const int first = xcd * per_xcd;
+    const int cnt = max(0, min(per_xcd, total - first));  // tiles of this XCD
+    int L = -1, half = -1;
+    if (TAIL) {
+      const int cpx = max(1, n_cu / kXcds), r = cnt % cpx;
+      const int nfull = (r > 0 && 2 * r <= cpx) ? cnt - r : cnt;
+      if (slot < nfull) {
+        L = first + slot;
+      } else if (slot < nfull + 2 * (cnt - nfull)) {
+        L = first + nfull + (slot - nfull) / 2;
+        half = (slot - nfull) & 1;
+      }
+    } else if (slot < cnt) {
+      L = first + slot;
+    }
     int res_e = -1, res_m = 0, res_n = 0, res_s = 0;
-    if (slot < per_xcd && L < total) {
+    if (L >= 0) {
       for (int e = 0; e < E; ++e) {
         const int m = offsets[e + 1] - offsets[e];
         const int mt = (m + BM - 1) / BM;
@@ -108,6 +130,7 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int
     s_tile[0] = res_e;
     s_tile[4] = res_s;
     s_tile[5] = S;
+    s_tile[6] = half;
     if (res_e >= 0) {
       const int m = offsets[res_e + 1] - offsets[res_e];
       s_tile[1] = offsets[res_e] + res_m * BM;
@@ -123,6 +146,7 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int
   out->rows = s_tile[2];
   out->nt = s_tile[3];
   out->ks = s_tile[4];
+  out->half = s_tile[6];
   return true;
 }
 
@@ -184,7 +208,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
   const int nk = (K + TK - 1) / TK;
-  __shared__ int s_tile[6];
+  __shared__ int s_tile[7];
   const bool have = map_tile<TM>(offsets, E, nN, max_split, n_cu, nk, &tile, s_tile);
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;
@@ -399,12 +423,13 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 // time, the pointer selection went through scratch memory). KMASK: the
 // reduction length is not a multiple of the step, so chunks past it read
 // the zero page.
+template <int V>
+using IntC = std::integral_constant<int, V>;
+
 constexpr int TM3 = 384;              // permuted rows per tile
 constexpr int STAGE_A3 = TM3 * TK * 2;  // 48 KB
 constexpr int NW3 = 8;
-constexpr int NINS = (TM3 + TW) / 8;  // 1 KB load instructions per stage (80)
-constexpr int IPW3 = NINS / NW3;      // 10
-constexpr int MBW = 3, NBW3 = 4;      // 32-row blocks per wave: tokens, weights
+constexpr int MBW = 3;                // 32-row token blocks per wave
 
 template <bool GATE_UP, bool KMASK>
 __global__ __launch_bounds__(NW3 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -423,8 +448,8 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
   const int nk = (K + TK - 1) / TK;
-  const bool have = map_tile<TM3>(offsets, E, nN, max_split, n_cu, nk, &tile,
-                                  reinterpret_cast<int*>(lds1a));
+  const bool have = map_tile<TM3, true>(offsets, E, nN, max_split, n_cu, nk, &tile,
+                                        reinterpret_cast<int*>(lds1a));
   __syncthreads();
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;
@@ -433,174 +458,185 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-
-  const int n0 = GATE_UP ? tile.nt * 128 : tile.nt * TW;
   const char* a_base = reinterpret_cast<const char*>(A);
   const size_t wexp = static_cast<size_t>(tile.e) * N * K * 2;
   const char* g_base = reinterpret_cast<const char*>(B0) + wexp;
   const char* u_base = reinterpret_cast<const char*>(GATE_UP ? B1 : B0) + wexp;
-  // instruction q = wave + 8 j: j < 6 are A instructions (q < 48: A rows
-  // 8q .. 8q+7), j >= 6 B instructions (B rows 8(wave + 8(j-6)) ..; for
-  // gate/up j = 6, 7 are gate rows and j = 8, 9 the same rows of up). Lane l
-  // writes row r = 8*qq + l/8, slot l%8, holding chunk (l%8) ^ ((r >> 1) & 7);
-  // (r >> 1) & 7 = (4*qq + l/16) & 7 = (4*wave + l/16) & 7 for every j.
-  constexpr int JA = TM3 / 8 / NW3;  // 6
-  const int ch = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-  uint32_t src_off[IPW3];
-#pragma unroll
-  for (int j = 0; j < IPW3; ++j) {
-    const bool isA = j < JA;
-    const int qq = isA ? wave + NW3 * j : wave + NW3 * (j - JA);
-    const int r = qq * 8 + (lane >> 3);
-    uint32_t row;
-    if (isA) {
-      const int rr = r < tile.rows ? r : r % tile.rows;
-      row = GATE_UP ? static_cast<uint32_t>(sorted_token[tile.row0 + rr])
-                    : static_cast<uint32_t>(tile.row0 + rr);
-    } else {
-      row = static_cast<uint32_t>(min(n0 + (GATE_UP ? (r & 127) : r), N - 1));
-    }
-    src_off[j] = row * static_cast<uint32_t>(K) * 2u + ch * 16u;
-  }
   const char* zero = reinterpret_cast<const char*>(g_zero_page);
   const __amdgpu_buffer_rsrc_t a_rs = buffer_rsrc(a_base), g_rs = buffer_rsrc(g_base),
                                u_rs = buffer_rsrc(u_base);
-  auto issue = [&](int kt, int st) {
-    const int k0 = kt * TK;
-    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
-    const bool kin = k0 + ch * 8 < K;
+  // (r >> 1) & 7 of every row a lane loads (see below) is (4*wave + l/16) & 7
+  const int ch = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  const int xr = ((lane & 31) >> 1) & 7, half = lane >> 5;
+  constexpr int JA = TM3 / 8 / NW3;  // 6 A load instructions per wave
+
+  // The tile with NB 32-row weight blocks per wave: NB = 4 for a whole
+  // column tile (256 weight rows), NB = 2 for a half one (128 rows; gate/up:
+  // 64 gate rows, then the same rows of up).
+  auto body = [&](auto nbc) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nbc)::value;
+    constexpr int WR = 64 * NB;    // weight rows of the tile
+    constexpr int IPW = JA + NB;   // load instructions per wave and stage
+    const int n0 = GATE_UP ? tile.nt * 128 + (NB == 2 ? 64 * tile.half : 0)
+                           : tile.nt * TW + (NB == 2 ? 128 * tile.half : 0);
+    // instruction q = wave + 8 j: j < JA are A instructions (A rows
+    // 8q .. 8q+7), j >= JA B instructions (B rows 8(wave + 8(j-JA)) ..; for
+    // gate/up the first half of them are gate rows, the second half the same
+    // rows of up). Lane l writes row r = 8*qq + l/8, slot l%8, holding chunk
+    // (l%8) ^ ((r >> 1) & 7).
+    uint32_t src_off[IPW];
 #pragma unroll
-    for (int j = 0; j < IPW3; ++j) {
+    for (int j = 0; j < IPW; ++j) {
       const bool isA = j < JA;
       const int qq = isA ? wave + NW3 * j : wave + NW3 * (j - JA);
-      const char* base = isA ? a_base : ((GATE_UP && j >= JA + 2) ? u_base : g_base);
-      load_lds16(kin ? base + (src_off[j] + kb) : zero, buf(st, isA ? 0 : 1) + qq * 1024);
+      const int r = qq * 8 + (lane >> 3);
+      uint32_t row;
+      if (isA) {
+        const int rr = r < tile.rows ? r : r % tile.rows;
+        row = GATE_UP ? static_cast<uint32_t>(sorted_token[tile.row0 + rr])
+                      : static_cast<uint32_t>(tile.row0 + rr);
+      } else {
+        row = static_cast<uint32_t>(min(n0 + (GATE_UP ? (r & (WR / 2 - 1)) : r), N - 1));
+      }
+      src_off[j] = row * static_cast<uint32_t>(K) * 2u + ch * 16u;
     }
-  };
-  const int xr = ((lane & 31) >> 1) & 7, half = lane >> 5;
-  int fa_off[MBW], fb_off[NBW3];
-#pragma unroll
-  for (int i = 0; i < MBW; ++i) fa_off[i] = (wm * 96 + i * 32 + (lane & 31)) * 128;
-#pragma unroll
-  for (int i = 0; i < NBW3; ++i) {
-    // gate/up: blocks 0,1 gate rows wn*64 + 32i, blocks 2,3 the same rows of up
-    const int brow = GATE_UP ? (i >> 1) * 128 + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
-    fb_off[i] = (brow + (lane & 31)) * 128;
-  }
-  f32x16 acc[NBW3][MBW];
-#pragma unroll
-  for (int a = 0; a < NBW3; ++a)
-#pragma unroll
-    for (int b = 0; b < MBW; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
-  // Load instruction j of step kt into stage st. Without KMASK every chunk
-  // of a step lies inside K: a buffer load from the operand's resource.
-  auto issue_j = [&](int kt, int st, int j) __attribute__((always_inline)) {
-    const int k0 = kt * TK;
-    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
-    const bool isA = j < JA;
-    const int qq = isA ? wave + NW3 * j : wave + NW3 * (j - JA);
-    const char* base = isA ? a_base : ((GATE_UP && j >= JA + 2) ? u_base : g_base);
-    char* dst = buf(st, isA ? 0 : 1) + qq * 1024;
-    if constexpr (KMASK) {
-      load_lds16(k0 + ch * 8 < K ? base + (src_off[j] + kb) : zero, dst);
-    } else {
-      buffer_load_lds16(isA ? a_rs : ((GATE_UP && j >= JA + 2) ? u_rs : g_rs), src_off[j], kb, dst);
-    }
-  };
-  // One step on stage st: 16 groups of one weight fragment times the three
-  // token fragments (3 MFMAs). The fragments of group g+1 are read before the
-  // MFMAs of group g, and the first kLoadGroups groups each issue a share of
-  // the next step's loads, so the load instructions go out at the rate the
-  // address unit takes them instead of stalling every wave at the start of
-  // the step; the scheduling fences keep that order. In the last step the
-  // loads re-read an in-range step into the idle stage, which keeps the
-  // instruction stream free of branches.
-  constexpr int kGroups = (TK / 16) * NBW3;  // 16
-  constexpr int kLoadGroups = 8;
-  auto step = [&](int kt, int st) __attribute__((always_inline)) {
-    const int kload = min(kt + 1, nk - 1);
-    auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
+    auto is_up = [&](int j) { return GATE_UP && j >= JA + NB / 2; };
+    // Load instruction j of step kt into stage st. Without KMASK every chunk
+    // of a step lies inside K: a buffer load from the operand's resource.
+    auto issue_j = [&](int kt, int st, int j, bool mask) __attribute__((always_inline)) {
+      const int k0 = kt * TK;
+      const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+      const bool isA = j < JA;
+      const int qq = isA ? wave + NW3 * j : wave + NW3 * (j - JA);
+      char* dst = buf(st, isA ? 0 : 1) + qq * 1024;
+      if (mask) {
+        const char* base = isA ? a_base : (is_up(j) ? u_base : g_base);
+        load_lds16(k0 + ch * 8 < K ? base + (src_off[j] + kb) : zero, dst);
+      } else {
+        buffer_load_lds16(isA ? a_rs : (is_up(j) ? u_rs : g_rs), src_off[j], kb, dst);
+      }
     };
-    bf16x8 fa[2][MBW], fb[2];
+    int fa_off[MBW], fb_off[NB];
 #pragma unroll
-    for (int i = 0; i < MBW; ++i) fa[0][i] = rd(0, fa_off[i], 0);
-    fb[0] = rd(1, fb_off[0], 0);
+    for (int i = 0; i < MBW; ++i) fa_off[i] = (wm * 96 + i * 32 + (lane & 31)) * 128;
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      const int s = g / NBW3, nb = g % NBW3, ca = s & 1, cb = g & 1;
-      if (g + 1 < kGroups) {
-        const int s1 = (g + 1) / NBW3, nb1 = (g + 1) % NBW3;
-        if (nb1 == 0) {
-#pragma unroll
-          for (int i = 0; i < MBW; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
-        }
-        fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
-      }
-      if (g < kLoadGroups) {
-#pragma unroll
-        for (int j = g * IPW3 / kLoadGroups; j < (g + 1) * IPW3 / kLoadGroups; ++j)
-          issue_j(kload, st ^ 1, j);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MBW; ++mb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < NB; ++i) {
+      // gate/up: blocks 0 .. NB/2-1 gate rows wn*WR/4 + 32i, then the same rows of up
+      const int brow = GATE_UP ? (i / (NB / 2)) * (WR / 2) + wn * (WR / 4) + (i % (NB / 2)) * 32
+                               : wn * (WR / 2) + i * 32;
+      fb_off[i] = (brow + (lane & 31)) * 128;
     }
-  };
-
-  const int nsteps = kend - kbeg;
-  if (nsteps > 0) issue(kbeg, 0);
-  for (int p = 0; p + 1 < nsteps; p += 2) {
+    f32x16 acc[NB][MBW];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int y = 0; y < MBW; ++y)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.f;
+
+    // One step on stage st: groups of one weight fragment times the three
+    // token fragments (3 MFMAs). The fragments of group g+1 are read before the
+    // MFMAs of group g, and the first half of the groups each issue a share of
+    // the next step's loads, so the load instructions go out at the rate the
+    // address unit takes them instead of stalling every wave at the start of
+    // the step; the scheduling fences keep that order. In the last step the
+    // loads re-read an in-range step into the idle stage, which keeps the
+    // instruction stream free of branches.
+    constexpr int kGroups = (TK / 16) * NB;
+    constexpr int kLoadGroups = kGroups / 2;
+    auto step = [&](int kt, int st) __attribute__((always_inline)) {
+      const int kload = min(kt + 1, nk - 1);
+      auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
+      };
+      bf16x8 fa[2][MBW], fb[2];
+#pragma unroll
+      for (int i = 0; i < MBW; ++i) fa[0][i] = rd(0, fa_off[i], 0);
+      fb[0] = rd(1, fb_off[0], 0);
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        const int s = g / NB, nb = g % NB, ca = s & 1, cb = g & 1;
+        if (g + 1 < kGroups) {
+          const int s1 = (g + 1) / NB, nb1 = (g + 1) % NB;
+          if (nb1 == 0) {
+#pragma unroll
+            for (int i = 0; i < MBW; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
+          }
+          fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
+        }
+        if (g < kLoadGroups) {
+#pragma unroll
+          for (int j = g * IPW / kLoadGroups; j < (g + 1) * IPW / kLoadGroups; ++j)
+            issue_j(kload, st ^ 1, j, KMASK);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    const int nsteps = kend - kbeg;
+    if (nsteps > 0) {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) issue_j(kbeg, 0, j, true);
+    }
+    for (int p = 0; p + 1 < nsteps; p += 2) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        step(kbeg + p + r, r);
+      }
+    }
+    if (nsteps & 1) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      step(kbeg + p + r, r);
+      step(kend - 1, 0);
     }
-  }
-  if (nsteps & 1) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    step(kend - 1, 0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    // acc[nb][mb] element i: token row wm*96 + mb*32 + lane%32, weight-tile
+    // row (block nb) + 8*(i/4) + 4*(lane/32) + i%4; gate block nb pairs with
+    // up block nb + NB/2.
 #pragma unroll
-  for (int mb = 0; mb < MBW; ++mb) {
-    const int m = wm * 96 + mb * 32 + (lane & 31);
-    if (m >= tile.rows) continue;
-    const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
+    for (int mb = 0; mb < MBW; ++mb) {
+      const int m = wm * 96 + mb * 32 + (lane & 31);
+      if (m >= tile.rows) continue;
+      const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int nloc = 8 * g + 4 * half;
-      if (GATE_UP) {
+      for (int g = 0; g < 4; ++g) {
+        const int nloc = 8 * g + 4 * half;
+        if (GATE_UP) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = tile.nt * 128 + wn * 64 + nb * 32 + nloc;
-          if (n < N) {
-            float hv[4];
+          for (int nb = 0; nb < NB / 2; ++nb) {
+            const int n = n0 + wn * (WR / 4) + nb * 32 + nloc;
+            if (n < N) {
+              float hv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + 2][mb][4 * g + i];
-            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+              for (int i = 0; i < 4; ++i)
+                hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + NB / 2][mb][4 * g + i];
+              *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
+                  make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            }
           }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int nb = 0; nb < NBW3; ++nb) {
-          const int n = tile.nt * TW + wn * 128 + nb * 32 + nloc;
-          if (n < N)
-            *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
-                make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
-                            acc[nb][mb][4 * g + 3]);
+          for (int nb = 0; nb < NB; ++nb) {
+            const int n = n0 + wn * (WR / 2) + nb * 32 + nloc;
+            if (n < N)
+              *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
+                  make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                              acc[nb][mb][4 * g + 3]);
+          }
         }
       }
     }
-  }
+  };
+  if (tile.half < 0)
+    body(IntC<4>{});
+  else
+    body(IntC<2>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -656,6 +692,11 @@ unsigned tile_grid(int rows, int E, int BM, int nN, int splits) {
   return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds);
 }
 
+// tile_grid plus the half-width tail tiles' extra slots (map_tile's TAIL)
+unsigned tall_grid(int rows, int E, int nN, int splits, int n_cu) {
+  return tile_grid(rows, E, TM3, nN, splits) + (n_cu / kXcds / 2) * kXcds;
+}
+
 // Tall tiles pay off once the experts average two tiles' worth of rows
 // (their padding is then at most a third of a tile over two or more).
 bool use_tall_tiles(int rows, int E) { return rows >= 2 * TM3 * E; }
@@ -684,9 +725,10 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
     return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows, h, s);
   if (use_tall_tiles(rows, E)) {
     auto kern = d % TK ? expert_gemm_tall_kernel<true, true> : expert_gemm_tall_kernel<true, false>;
-    kern<<<tile_grid(rows, E, TM3, (ffn + 127) / 128, 1), NW3 * 64, 0, s>>>(
+    const int ncu = cu_count();
+    kern<<<tall_grid(rows, E, (ffn + 127) / 128, 1, ncu), NW3 * 64, 0, s>>>(
         static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
-        static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
+        static_cast<const bf16_t*>(w_up), ffn, d, h, 1, ncu, 0, nullptr);
     return launch_status();
   }
   auto kern = d % TK ? expert_gemm_bf16_kernel<true, kWaves, true> : expert_gemm_bf16_kernel<true, kWaves, false>;
@@ -709,9 +751,10 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
   if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, rows, y, split, s);
   if (use_tall_tiles(rows, E)) {
     auto kern = ffn % TK ? expert_gemm_tall_kernel<false, true> : expert_gemm_tall_kernel<false, false>;
-    kern<<<tile_grid(rows, E, TM3, (d + TW - 1) / TW, kMaxDownSplit), NW3 * 64, 0, s>>>(
+    const int ncu = cu_count();
+    kern<<<tall_grid(rows, E, (d + TW - 1) / TW, kMaxDownSplit, ncu), NW3 * 64, 0, s>>>(
         static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
-        nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
+        nullptr, d, ffn, y, kMaxDownSplit, ncu, static_cast<size_t>(rows) * d, split);
     return launch_status();
   }
   auto kern = ffn % TK ? expert_gemm_bf16_kernel<false, kWaves, true> : expert_gemm_bf16_kernel<false, kWaves, false>;
