@@ -415,9 +415,10 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 // lane), two 80 KB LDS stages (the whole LDS). Each step moves 80 KB into the
 // CU for 12.6 MFLOP, 17% fewer bytes per FLOP than the 256 x 256 tile; the
 // cost is coarser row padding, so the host takes these tiles only when the
-// experts average at least two tiles' worth of rows. Same swizzle, stages
-// and epilogue as the 256 x 256 kernel, but the next step's loads are spread
-// over the first half of each step (see step below). Which operand and
+// experts average at least two tiles' worth of rows. The tiles of an XCD's
+// last, at most half-full round run at half width (384 x 128, 96 x 64 per
+// wave; see map_tile's TAIL). Same swizzle, stages and epilogue as the
+// 256 x 256 kernel. Which operand and
 // which weight matrix each load instruction serves is fixed per unrolled
 // index, so the compiler keeps the choice in scalar code (chosen at run
 // time, the pointer selection went through scratch memory). KMASK: the
