@@ -62,7 +62,9 @@ struct Tile {
   int half;   // -1: the whole column tile; 0 or 1: that half of its weight rows
 };
 
-// Map this workgroup to a tile of BM rows; returns false if it has none.
+// Tile of workgroup `block` among tiles of BM rows: res = {expert (-1:
+// none), first permuted row, rows, column tile, split part, split count S,
+// half (-1: whole column tile; 0 or 1: that half of its weight rows)}.
 // With max_split > 1 the reduction dimension may be cut into S <= max_split
 // parts, each a separate tile whose partial result goes to its own output
 // slice; S is chosen from the real tile count to minimise the number of
@@ -74,70 +76,72 @@ struct Tile {
 // half-width tiles, so its last round takes about half a tile's time
 // instead of a whole one (the workgroups of the halves come last in the
 // XCD's order); the grid provides n_cu/16 extra slots per XCD for them.
-// s_tile: seven ints of LDS for broadcasting the result from thread 0.
+// Host-callable so that the assignment can be checked exhaustively on the
+// CPU.
+template <int BM, bool TAIL>
+__host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets, int E, int nN,
+                                            int max_split, int n_cu, int nk, int block, int* res) {
+  int base = 0;
+  for (int e = 0; e < E; ++e) {
+    const int m = offsets[e + 1] - offsets[e];
+    base += ((m + BM - 1) / BM) * nN;
+  }
+  int S = 1, best_rounds = (base + n_cu - 1) / n_cu;  // rounds of S-tiles
+  for (int c = 2; c <= max_split && c * kMinSplitSteps <= nk; ++c) {
+    const int rounds = (base * c + n_cu - 1) / n_cu;
+    if (rounds * S < best_rounds * c) {  // rounds/c < best_rounds/S
+      S = c;
+      best_rounds = rounds;
+    }
+  }
+  const int total = base * S;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int xcd = block % kXcds, slot = block / kXcds;
+  const int first = xcd * per_xcd;
+  int cnt = total - first;  // tiles of this XCD
+  cnt = cnt < 0 ? 0 : (cnt > per_xcd ? per_xcd : cnt);
+  int L = -1, half = -1;
+  if (TAIL) {
+    const int cpx = n_cu / kXcds > 1 ? n_cu / kXcds : 1, r = cnt % cpx;
+    const int nfull = (r > 0 && 2 * r <= cpx) ? cnt - r : cnt;
+    if (slot < nfull) {
+      L = first + slot;
+    } else if (slot < nfull + 2 * (cnt - nfull)) {
+      L = first + nfull + (slot - nfull) / 2;
+      half = (slot - nfull) & 1;
+    }
+  } else if (slot < cnt) {
+    L = first + slot;
+  }
+  res[0] = -1;
+  res[5] = S;
+  res[6] = half;
+  if (L < 0) return;
+  for (int e = 0; e < E; ++e) {
+    const int m = offsets[e + 1] - offsets[e];
+    const int mt = (m + BM - 1) / BM;
+    const int te = mt * nN;  // tiles of one split of expert e
+    if (L < te * S) {
+      const int ks = L / te;
+      L -= ks * te;
+      const int mi = L % mt;
+      res[0] = e;
+      res[1] = offsets[e] + mi * BM;
+      res[2] = m - mi * BM < BM ? m - mi * BM : BM;
+      res[3] = L / mt;
+      res[4] = ks;
+      return;
+    }
+    L -= te * S;
+  }
+}
+
+// Map this workgroup to its tile (assign_tile, computed by thread 0);
+// returns false if it has none. s_tile: seven ints of LDS.
 template <int BM, bool TAIL = false>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
                          int n_cu, int nk, Tile* out, int* s_tile) {
-  if (threadIdx.x == 0) {
-    int base = 0;
-    for (int e = 0; e < E; ++e) {
-      const int m = offsets[e + 1] - offsets[e];
-      base += ((m + BM - 1) / BM) * nN;
-    }
-    int S = 1, best_rounds = (base + n_cu - 1) / n_cu;  // rounds of S-tiles
-    for (int c = 2; c <= max_split && c * kMinSplitSteps <= nk; ++c) {
-      const int rounds = (base * c + n_cu - 1) / n_cu;
-      if (rounds * S < best_rounds * c) {  // rounds/c < best_rounds/S
-        S = c;
-        best_rounds = rounds;
-      }
-    }
-    const int total = base * S;
-    const int per_xcd = (total + kXcds - 1) / kXcds;
-    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    const int first = xcd * per_xcd;
-    const int cnt = max(0, min(per_xcd, total - first));  // tiles of this XCD
-    int L = -1, half = -1;
-    if (TAIL) {
-      const int cpx = max(1, n_cu / kXcds), r = cnt % cpx;
-      const int nfull = (r > 0 && 2 * r <= cpx) ? cnt - r : cnt;
-      if (slot < nfull) {
-        L = first + slot;
-      } else if (slot < nfull + 2 * (cnt - nfull)) {
-        L = first + nfull + (slot - nfull) / 2;
-        half = (slot - nfull) & 1;
-      }
-    } else if (slot < cnt) {
-      L = first + slot;
-    }
-    int res_e = -1, res_m = 0, res_n = 0, res_s = 0;
-    if (L >= 0) {
-      for (int e = 0; e < E; ++e) {
-        const int m = offsets[e + 1] - offsets[e];
-        const int mt = (m + BM - 1) / BM;
-        const int te = mt * nN;  // tiles of one split of expert e
-        if (L < te * S) {
-          res_s = L / te;
-          L -= res_s * te;
-          res_e = e;
-          res_n = L / mt;
-          res_m = L % mt;
-          break;
-        }
-        L -= te * S;
-      }
-    }
-    s_tile[0] = res_e;
-    s_tile[4] = res_s;
-    s_tile[5] = S;
-    s_tile[6] = half;
-    if (res_e >= 0) {
-      const int m = offsets[res_e + 1] - offsets[res_e];
-      s_tile[1] = offsets[res_e] + res_m * BM;
-      s_tile[2] = min(BM, m - res_m * BM);
-      s_tile[3] = res_n;
-    }
-  }
+  if (threadIdx.x == 0) assign_tile<BM, TAIL>(offsets, E, nN, max_split, n_cu, nk, blockIdx.x, s_tile);
   __syncthreads();
   out->S = s_tile[5];
   if (s_tile[0] < 0) return false;

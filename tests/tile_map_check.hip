@@ -1,0 +1,86 @@
+// CPU check of the grouped GEMMs' tile assignment (assign_tile): over many
+// random expert-count patterns, shapes, split limits and CU counts, every
+// tile of every expert (and split part) is handed to exactly one workgroup
+// of the launched grid, whole or as both of its halves, and nothing else is.
+// Built and run by test_tile_map.py; needs no GPU.
+#include "../sparse_mixture_experts_renorm_amd/csrc/expert_gemm.hip"
+#include "../sparse_mixture_experts_renorm_amd/csrc/expert_stream.hip"
+
+#include <cstdio>
+#include <map>
+#include <random>
+#include <tuple>
+#include <vector>
+
+using namespace moe;
+
+template <int BM, bool TAIL>
+static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN, int max_split,
+                 int n_cu, int nk, long long* tiles_seen) {
+  const unsigned grid = TAIL ? tall_grid(rows_bound, E, nN, max_split, n_cu)
+                             : tile_grid(rows_bound, E, BM, nN, max_split);
+  // key (e, row tile, column tile, part) -> counts {whole, half 0, half 1}
+  std::map<std::tuple<int, int, int, int>, std::array<int, 3>> seen;
+  int S = -1;
+  for (unsigned b = 0; b < grid; ++b) {
+    int res[7];
+    assign_tile<BM, TAIL>(off.data(), E, nN, max_split, n_cu, nk, static_cast<int>(b), res);
+    if (S < 0) S = res[5];
+    if (res[5] != S) return printf("split count differs between workgroups\n"), 1;
+    if (res[0] < 0) continue;
+    const int e = res[0], m = off[e + 1] - off[e], mi = (res[1] - off[e]) / BM;
+    if (e >= E || res[1] != off[e] + mi * BM || mi < 0 || res[2] != std::min(BM, m - mi * BM) ||
+        res[2] <= 0 || res[3] < 0 || res[3] >= nN || res[4] < 0 || res[4] >= S ||
+        res[6] < -1 || res[6] > 1 || (!TAIL && res[6] != -1))
+      return printf("bad tile: e %d row0 %d rows %d nt %d ks %d half %d\n", e, res[1], res[2],
+                    res[3], res[4], res[6]), 1;
+    seen[{e, mi, res[3], res[4]}][res[6] + 1] += 1;
+  }
+  long long expected = 0;
+  for (int e = 0; e < E; ++e) expected += static_cast<long long>((off[e + 1] - off[e] + BM - 1) / BM);
+  expected *= static_cast<long long>(nN) * (S < 1 ? 1 : S);
+  if (static_cast<long long>(seen.size()) != expected)
+    return printf("%zu distinct tiles assigned, %lld expected (grid %u)\n", seen.size(), expected, grid), 1;
+  for (const auto& kv : seen) {
+    const auto& c = kv.second;
+    // c[0]: whole (half -1), c[1], c[2]: halves 0 and 1
+    const bool whole = c[0] == 1 && c[1] == 0 && c[2] == 0;
+    const bool halves = c[0] == 0 && c[1] == 1 && c[2] == 1;
+    if (!whole && !halves)
+      return printf("tile assigned %d whole, %d + %d halves\n", c[0], c[1], c[2]), 1;
+  }
+  *tiles_seen += expected;
+  return 0;
+}
+
+int main() {
+  std::mt19937 rng(12345);
+  long long tiles = 0;
+  int cases = 0;
+  const int cus[] = {256, 304, 80, 8, 1};
+  for (int it = 0; it < 3000; ++it) {
+    const int E = 1 + static_cast<int>(rng() % 64);
+    std::vector<int32_t> off(E + 1, 0);
+    for (int e = 0; e < E; ++e) {
+      int m;
+      switch (it % 5) {
+        case 0: m = static_cast<int>(rng() % 3000); break;                         // anything
+        case 1: m = (rng() % 3 == 0) ? 0 : 700 + static_cast<int>(rng() % 700);    // some empty
+        case 2: m = e == 0 ? 20000 + static_cast<int>(rng() % 9000) : static_cast<int>(rng() % 60);
+        case 3: m = 384 * static_cast<int>(rng() % 5) + 128 * static_cast<int>(rng() % 3);
+        default: m = static_cast<int>(rng() % 40); break;                          // decode-like
+      }
+      off[e + 1] = off[e] + m;
+    }
+    const int rows_bound = off[E] + static_cast<int>(rng() % 50);  // capacity may keep fewer
+    const int nN = 1 + static_cast<int>(rng() % 130);
+    const int max_split = (it & 1) ? kMaxDownSplit : 1;
+    const int nk = 1 + static_cast<int>(rng() % 400);
+    const int n_cu = cus[it % 5];
+    if (check<256, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
+    if (check<384, true>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
+    cases += 2;
+  }
+  printf("ok: %d cases, %lld tiles\n", cases, tiles);
+  return 0;
+}
