@@ -62,9 +62,24 @@ struct Tile {
   int half;   // -1: the whole column tile; 0 or 1: that half of its weight rows
 };
 
-// Tile of workgroup `block` among tiles of BM rows: res = {expert (-1:
-// none), first permuted row, rows, column tile, split part, split count S,
-// half (-1: whole column tile; 0 or 1: that half of its weight rows)}.
+// Row tiles of BM rows per expert, as a prefix: pref[e] = sum over e' < e of
+// ceil(M_e' / BM), for e = 0 .. E (M_e = offsets[e+1] - offsets[e]).
+// Serial form, for the host; the kernels build the same array with one wave
+// (map_tile).
+template <int BM>
+__host__ __device__ inline void row_tile_prefix(const int32_t* __restrict__ offsets, int E,
+                                                int* pref) {
+  pref[0] = 0;
+  for (int e = 0; e < E; ++e) pref[e + 1] = pref[e] + (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+}
+
+// Tile of workgroup `block` among tiles of BM rows, given the experts' row
+// offsets and their row-tile prefix pref [E+1]: res = {expert (-1: none),
+// first permuted row, rows, column tile, split part, split count S, half
+// (-1: whole column tile; 0 or 1: that half of its weight rows)}.
+// The tile list runs over the experts in order; inside an expert over the
+// split parts, and inside a part over column tiles and, for each, over its
+// row tiles.
 // With max_split > 1 the reduction dimension may be cut into S <= max_split
 // parts, each a separate tile whose partial result goes to its own output
 // slice; S is chosen from the real tile count to minimise the number of
@@ -79,13 +94,10 @@ struct Tile {
 // Host-callable so that the assignment can be checked exhaustively on the
 // CPU.
 template <int BM, bool TAIL>
-__host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets, int E, int nN,
-                                            int max_split, int n_cu, int nk, int block, int* res) {
-  int base = 0;
-  for (int e = 0; e < E; ++e) {
-    const int m = offsets[e + 1] - offsets[e];
-    base += ((m + BM - 1) / BM) * nN;
-  }
+__host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets, const int* pref,
+                                            int E, int nN, int max_split, int n_cu, int nk,
+                                            int block, int* res) {
+  const int base = pref[E] * nN;
   int S = 1, best_rounds = (base + n_cu - 1) / n_cu;  // rounds of S-tiles
   for (int c = 2; c <= max_split && c * kMinSplitSteps <= nk; ++c) {
     const int rounds = (base * c + n_cu - 1) / n_cu;
@@ -117,40 +129,74 @@ __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets,
   res[5] = S;
   res[6] = half;
   if (L < 0) return;
-  for (int e = 0; e < E; ++e) {
-    const int m = offsets[e + 1] - offsets[e];
-    const int mt = (m + BM - 1) / BM;
-    const int te = mt * nN;  // tiles of one split of expert e
-    if (L < te * S) {
-      const int ks = L / te;
-      L -= ks * te;
-      const int mi = L % mt;
-      res[0] = e;
-      res[1] = offsets[e] + mi * BM;
-      res[2] = m - mi * BM < BM ? m - mi * BM : BM;
-      res[3] = L / mt;
-      res[4] = ks;
-      return;
-    }
-    L -= te * S;
+  // the expert of tile L: the first e with pref[e+1] * nN * S > L
+  const int per_row_tile = nN * S;
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pref[mid + 1] * per_row_tile > L) hi = mid; else lo = mid + 1;
   }
+  const int e = lo;
+  L -= pref[e] * per_row_tile;
+  const int mt = pref[e + 1] - pref[e], m = offsets[e + 1] - offsets[e];
+  const int te = mt * nN;  // tiles of one split part of expert e
+  const int ks = L / te;
+  L -= ks * te;
+  const int mi = L % mt;
+  res[0] = e;
+  res[1] = offsets[e] + mi * BM;
+  res[2] = m - mi * BM < BM ? m - mi * BM : BM;
+  res[3] = L / mt;
+  res[4] = ks;
 }
 
-// Map this workgroup to its tile (assign_tile, computed by thread 0);
-// returns false if it has none. s_tile: seven ints of LDS.
+// LDS the tile map needs: the seven results, then the prefix.
+constexpr int kMapLdsInts = 8 + kMaxExperts + 1;
+static_assert(kMaxExperts <= 4 * kWave, "map_tile sums four experts per lane");
+
+// Map this workgroup to its tile; returns false if it has none. Wave 0
+// builds the row-tile prefix in LDS (lane l sums experts 4l .. 4l+3, a wave
+// scan adds up the lanes: one memory round trip for any E <= 256), then
+// thread 0 runs assign_tile on it. s_map: kMapLdsInts ints of LDS.
 template <int BM, bool TAIL = false>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
-                         int n_cu, int nk, Tile* out, int* s_tile) {
-  if (threadIdx.x == 0) assign_tile<BM, TAIL>(offsets, E, nN, max_split, n_cu, nk, blockIdx.x, s_tile);
+                         int n_cu, int nk, Tile* out, int* s_map) {
+  int* pref = s_map + 8;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      c[q] = e < E ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+      sum += c[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int dl = 1; dl < kWave; dl <<= 1) {
+      const int v = __shfl_up(incl, dl, kWave);
+      if (lane >= dl) incl += v;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      if (e < E) pref[e] = run;
+      run += c[q];
+    }
+    if (lane == kWave - 1) pref[E] = incl;
+  }
   __syncthreads();
-  out->S = s_tile[5];
-  if (s_tile[0] < 0) return false;
-  out->e = s_tile[0];
-  out->row0 = s_tile[1];
-  out->rows = s_tile[2];
-  out->nt = s_tile[3];
-  out->ks = s_tile[4];
-  out->half = s_tile[6];
+  if (threadIdx.x == 0) assign_tile<BM, TAIL>(offsets, pref, E, nN, max_split, n_cu, nk, blockIdx.x, s_map);
+  __syncthreads();
+  out->S = s_map[5];
+  if (s_map[0] < 0) return false;
+  out->e = s_map[0];
+  out->row0 = s_map[1];
+  out->rows = s_map[2];
+  out->nt = s_map[3];
+  out->ks = s_map[4];
+  out->half = s_map[6];
   return true;
 }
 
@@ -212,8 +258,8 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
   const int nk = (K + TK - 1) / TK;
-  __shared__ int s_tile[7];
-  const bool have = map_tile<TM>(offsets, E, nN, max_split, n_cu, nk, &tile, s_tile);
+  __shared__ int s_map[kMapLdsInts];
+  const bool have = map_tile<TM>(offsets, E, nN, max_split, n_cu, nk, &tile, s_map);
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;
   // reduction steps [kbeg, kend) of this tile
@@ -395,7 +441,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
             float hv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + NBW / 2][mb][4 * g + i];
+              hv[i] = silu_fast(acc[nb][mb][4 * g + i]) * acc[nb + NBW / 2][mb][4 * g + i];
             *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
                 make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
           }
@@ -620,7 +666,7 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
               float hv[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                hv[i] = silu(acc[nb][mb][4 * g + i]) * acc[nb + NB / 2][mb][4 * g + i];
+                hv[i] = silu_fast(acc[nb][mb][4 * g + i]) * acc[nb + NB / 2][mb][4 * g + i];
               *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
                   make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
             }

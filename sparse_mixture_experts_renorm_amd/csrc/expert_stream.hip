@@ -159,7 +159,7 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
       if (GATE_UP) {
         float hv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = silu(accg[r][t][i]) * accu[r][t][i];
+        for (int i = 0; i < 4; ++i) hv[i] = silu_fast(accg[r][t][i]) * accu[r][t][i];
         *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
             make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
       } else {

@@ -125,6 +125,10 @@ EXPERT_SHAPES = [
     # reduction and the last step of each part reads past K
     (1600, 256, 6160, 2, 1, "bf16", "random"),   # tall tiles
     (600, 128, 6160, 2, 1, "bf16", "random"),    # 256 x 256 tiles
+    # many experts: the tile map's prefix over up to 256 experts (four per lane)
+    (4000, 64, 128, 256, 4, "bf16", "random"),   # 256 x 256 tiles, E at the limit
+    (3000, 64, 96, 130, 8, "bf16", "random"),    # E not a multiple of four
+    (9600, 64, 96, 100, 8, "bf16", "random"),    # tall tiles
 ]
 
 

@@ -1,5 +1,6 @@
-// CPU check of the grouped GEMMs' tile assignment (assign_tile): over many
-// random expert-count patterns, shapes, split limits and CU counts, every
+// CPU check of the grouped GEMMs' tile assignment (assign_tile on the
+// row-tile prefix): over many random expert-count patterns (up to 256
+// experts), shapes, split limits and CU counts, every
 // tile of every expert (and split part) is handed to exactly one workgroup
 // of the launched grid, whole or as both of its halves, and nothing else is.
 // Built and run by test_tile_map.py; needs no GPU.
@@ -22,9 +23,11 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
   // key (e, row tile, column tile, part) -> counts {whole, half 0, half 1}
   std::map<std::tuple<int, int, int, int>, std::array<int, 3>> seen;
   int S = -1;
+  std::vector<int> pref(E + 1);
+  row_tile_prefix<BM>(off.data(), E, pref.data());
   for (unsigned b = 0; b < grid; ++b) {
     int res[7];
-    assign_tile<BM, TAIL>(off.data(), E, nN, max_split, n_cu, nk, static_cast<int>(b), res);
+    assign_tile<BM, TAIL>(off.data(), pref.data(), E, nN, max_split, n_cu, nk, static_cast<int>(b), res);
     if (S < 0) S = res[5];
     if (res[5] != S) return printf("split count differs between workgroups\n"), 1;
     if (res[0] < 0) continue;
@@ -59,7 +62,7 @@ int main() {
   int cases = 0;
   const int cus[] = {256, 304, 80, 8, 1};
   for (int it = 0; it < 3000; ++it) {
-    const int E = 1 + static_cast<int>(rng() % 64);
+    const int E = 1 + static_cast<int>(rng() % (it % 7 == 0 ? kMaxExperts : 64));
     std::vector<int32_t> off(E + 1, 0);
     for (int e = 0; e < E; ++e) {
       int m;
