@@ -224,6 +224,9 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds_chunk_base), 16, voff, soff, 0, 0);
 }
 
+template <int V>
+using IntC = std::integral_constant<int, V>;
+
 constexpr int TM = 256;        // permuted rows per tile
 constexpr int TW = 256;        // weight rows per tile
 constexpr int TK = 64;         // reduction step (elements); one LDS row = 128 bytes
@@ -333,7 +336,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // rows of up (tile rows + 128); down: NBW consecutive blocks
   int fa_off[4], fb_off[NBW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa_off[i] = (wm * 128 + i * 32 + (lane & 31)) * 128;
+  for (int i = 0; i < 4; ++i) fa_off[i] = ((wm + 2 * i) * 32 + (lane & 31)) * 128;
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     const int brow = GATE_UP ? (i / (NBW / 2)) * 128 + wn * (NBW / 2) * 32 + (i % (NBW / 2)) * 32
@@ -359,75 +362,93 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // instruction stream free of branches.
   constexpr int kGroups = (TK / 16) * NBW;
   constexpr int kLoadGroups = kGroups / 2;
-  auto step = [&](int kt, int st) __attribute__((always_inline)) {
-    const int kload = min(kt + 1, nk - 1);
-    auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
-    };
-    bf16x8 fa[2][4], fb[2];
+  auto run = [&](auto mac) __attribute__((always_inline)) {
+    constexpr int MA = decltype(mac)::value;  // token blocks of this wave with real rows
+    auto step = [&](int kt, int st) __attribute__((always_inline)) {
+      const int kload = min(kt + 1, nk - 1);
+      auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
+      };
+      bf16x8 fa[2][MA], fb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = rd(0, fa_off[i], 0);
-    fb[0] = rd(1, fb_off[0], 0);
+      for (int i = 0; i < MA; ++i) fa[0][i] = rd(0, fa_off[i], 0);
+      fb[0] = rd(1, fb_off[0], 0);
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      const int s = g / NBW, nb = g % NBW, ca = s & 1, cb = g & 1;
-      if (g + 1 < kGroups) {
-        const int s1 = (g + 1) / NBW, nb1 = (g + 1) % NBW;
-        if (nb1 == 0) {
+      for (int g = 0; g < kGroups; ++g) {
+        const int s = g / NBW, nb = g % NBW, ca = s & 1, cb = g & 1;
+        if (g + 1 < kGroups) {
+          const int s1 = (g + 1) / NBW, nb1 = (g + 1) % NBW;
+          if (nb1 == 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
+            for (int i = 0; i < MA; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
+          }
+          fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
         }
-        fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
-      }
-      if (g < kLoadGroups) {
+        if (g < kLoadGroups) {
 #pragma unroll
-        for (int j = g * 2 * IPW / kLoadGroups; j < (g + 1) * 2 * IPW / kLoadGroups; ++j)
-          issue_one(kload, st ^ 1, j);
-      }
+          for (int j = g * 2 * IPW / kLoadGroups; j < (g + 1) * 2 * IPW / kLoadGroups; ++j)
+            issue_one(kload, st ^ 1, j);
+        }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
+        for (int mb = 0; mb < MA; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
 
-  // Before step kt is computed its loads must have landed in LDS (each wave
-  // waits for its own); the barrier then makes every wave's loads visible
-  // and guarantees that the other stage, overwritten during step kt, is no
-  // longer read. Steps go in pairs (stage 0, stage 1); an odd last step runs
-  // on stage 0.
-  const int nsteps = kend - kbeg;
-  if (nsteps > 0) {
-    const int k0 = kbeg * TK;
+    // Before step kt is computed its loads must have landed in LDS (each wave
+    // waits for its own); the barrier then makes every wave's loads visible
+    // and guarantees that the other stage, overwritten during step kt, is no
+    // longer read. Steps go in pairs (stage 0, stage 1); an odd last step runs
+    // on stage 0.
+    const int nsteps = kend - kbeg;
+    if (nsteps > 0) {
+      const int k0 = kbeg * TK;
 #pragma unroll
-    for (int j = 0; j < 2 * IPW; ++j) {
-      const int jj = j % IPW;
-      const bool kin = k0 + kchunk[jj] * 8 < K;
-      const char* src = j < IPW ? a_base + (a_off[jj] + k0 * 2u) : b_base[jj] + (b_off[jj] + k0 * 2u);
-      load_lds16(kin ? src : zero, buf(0, j < IPW ? 0 : 1) + (wave * IPW + jj) * 1024);
+      for (int j = 0; j < 2 * IPW; ++j) {
+        const int jj = j % IPW;
+        const bool kin = k0 + kchunk[jj] * 8 < K;
+        const char* src = j < IPW ? a_base + (a_off[jj] + k0 * 2u) : b_base[jj] + (b_off[jj] + k0 * 2u);
+        load_lds16(kin ? src : zero, buf(0, j < IPW ? 0 : 1) + (wave * IPW + jj) * 1024);
+      }
     }
-  }
-  for (int p = 0; p + 1 < nsteps; p += 2) {
+    for (int p = 0; p + 1 < nsteps; p += 2) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < 2; ++r) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        step(kbeg + p + r, r);
+      }
+    }
+    if (nsteps & 1) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      step(kbeg + p + r, r);
+      step(kend - 1, 0);
     }
-  }
-  if (nsteps & 1) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    step(kend - 1, 0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  // Token block i of this wave is tile block wm + 2i (32 rows each), so the
+  // blocks past the tile's rows fall on the waves, and so on the SIMDs,
+  // about equally; a wave runs the step with only its MA blocks that hold
+  // rows (the MFMAs of padding blocks are skipped). Every variant loads the
+  // same data and meets the same barriers.
+  const int nblk = (tile.rows + 31) / 32;
+  const int nact = nblk - wm >= 7 ? 4 : (nblk - wm >= 5 ? 3 : (nblk - wm >= 3 ? 2 : 1));
+  if (nact == 4)
+    run(IntC<4>{});
+  else if (nact == 3)
+    run(IntC<3>{});
+  else if (nact == 2)
+    run(IntC<2>{});
+  else
+    run(IntC<1>{});
 
-  // ---- epilogue. acc[nb][mb] element i: token row wm*128 + mb*32 + lane%32,
+  // ---- epilogue. acc[nb][mb] element i: token row (wm + 2 mb)*32 + lane%32,
   // weight-tile row (block nb) + 8*(i/4) + 4*(lane/32) + i%4. Gate block nb
   // pairs with up block nb + NBW/2.
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int m = wm * 128 + mb * 32 + (lane & 31);
+    const int m = (wm + 2 * mb) * 32 + (lane & 31);
     if (m >= tile.rows) continue;
     const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
 #pragma unroll
@@ -462,7 +483,8 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 
 // Tall tiles: 384 permuted rows x 256 weight rows, 8 waves (two per SIMD) of
 // 96 x 128 (3 x 4 accumulators of v_mfma_f32_32x32x16_bf16, 192 fp32 per
-// lane), two 80 KB LDS stages (the whole LDS). Each step moves 80 KB into the
+// lane; the wave's three 32-row blocks are tile blocks wm, wm + 4, wm + 8),
+// two 80 KB LDS stages (the whole LDS). Each step moves 80 KB into the
 // CU for 12.6 MFLOP, 17% fewer bytes per FLOP than the 256 x 256 tile; the
 // cost is coarser row padding, so the host takes these tiles only when the
 // experts average at least two tiles' worth of rows. The tiles of an XCD's
@@ -474,9 +496,6 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 // time, the pointer selection went through scratch memory). KMASK: the
 // reduction length is not a multiple of the step, so chunks past it read
 // the zero page.
-template <int V>
-using IntC = std::integral_constant<int, V>;
-
 constexpr int TM3 = 384;              // permuted rows per tile
 constexpr int STAGE_A3 = TM3 * TK * 2;  // 48 KB
 constexpr int NW3 = 8;
@@ -569,7 +588,7 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
     };
     int fa_off[MBW], fb_off[NB];
 #pragma unroll
-    for (int i = 0; i < MBW; ++i) fa_off[i] = (wm * 96 + i * 32 + (lane & 31)) * 128;
+    for (int i = 0; i < MBW; ++i) fa_off[i] = ((wm + 4 * i) * 32 + (lane & 31)) * 128;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       // gate/up: blocks 0 .. NB/2-1 gate rows wn*WR/4 + 32i, then the same rows of up
@@ -595,64 +614,81 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
     // instruction stream free of branches.
     constexpr int kGroups = (TK / 16) * NB;
     constexpr int kLoadGroups = kGroups / 2;
-    auto step = [&](int kt, int st) __attribute__((always_inline)) {
-      const int kload = min(kt + 1, nk - 1);
-      auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
-        return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
-      };
-      bf16x8 fa[2][MBW], fb[2];
+    auto run = [&](auto mac) __attribute__((always_inline)) {
+      constexpr int MA = decltype(mac)::value;  // token blocks of this wave with real rows
+      auto step = [&](int kt, int st) __attribute__((always_inline)) {
+        const int kload = min(kt + 1, nk - 1);
+        auto rd = [&](int op, int off, int s) __attribute__((always_inline)) {
+          return *reinterpret_cast<const bf16x8*>(buf(st, op) + off + (((2 * s + half) ^ xr) << 4));
+        };
+        bf16x8 fa[2][MA], fb[2];
 #pragma unroll
-      for (int i = 0; i < MBW; ++i) fa[0][i] = rd(0, fa_off[i], 0);
-      fb[0] = rd(1, fb_off[0], 0);
+        for (int i = 0; i < MA; ++i) fa[0][i] = rd(0, fa_off[i], 0);
+        fb[0] = rd(1, fb_off[0], 0);
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        const int s = g / NB, nb = g % NB, ca = s & 1, cb = g & 1;
-        if (g + 1 < kGroups) {
-          const int s1 = (g + 1) / NB, nb1 = (g + 1) % NB;
-          if (nb1 == 0) {
+        for (int g = 0; g < kGroups; ++g) {
+          const int s = g / NB, nb = g % NB, ca = s & 1, cb = g & 1;
+          if (g + 1 < kGroups) {
+            const int s1 = (g + 1) / NB, nb1 = (g + 1) % NB;
+            if (nb1 == 0) {
 #pragma unroll
-            for (int i = 0; i < MBW; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
+              for (int i = 0; i < MA; ++i) fa[ca ^ 1][i] = rd(0, fa_off[i], s1);
+            }
+            fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
           }
-          fb[cb ^ 1] = rd(1, fb_off[nb1], s1);
-        }
-        if (g < kLoadGroups) {
+          if (g < kLoadGroups) {
 #pragma unroll
-          for (int j = g * IPW / kLoadGroups; j < (g + 1) * IPW / kLoadGroups; ++j)
-            issue_j(kload, st ^ 1, j, KMASK);
-        }
+            for (int j = g * IPW / kLoadGroups; j < (g + 1) * IPW / kLoadGroups; ++j)
+              issue_j(kload, st ^ 1, j, KMASK);
+          }
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
+          for (int mb = 0; mb < MA; ++mb)
+            acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cb], fa[ca][mb], acc[nb][mb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
 
-    const int nsteps = kend - kbeg;
-    if (nsteps > 0) {
+      const int nsteps = kend - kbeg;
+      if (nsteps > 0) {
 #pragma unroll
-      for (int j = 0; j < IPW; ++j) issue_j(kbeg, 0, j, true);
-    }
-    for (int p = 0; p + 1 < nsteps; p += 2) {
+        for (int j = 0; j < IPW; ++j) issue_j(kbeg, 0, j, true);
+      }
+      for (int p = 0; p + 1 < nsteps; p += 2) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < 2; ++r) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          step(kbeg + p + r, r);
+        }
+      }
+      if (nsteps & 1) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        step(kbeg + p + r, r);
+        step(kend - 1, 0);
       }
-    }
-    if (nsteps & 1) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      step(kend - 1, 0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    // Token block i of this wave is tile block wm + 4i (32 rows each), so the
+    // blocks past the tile's rows (an expert's last row tile) fall on every
+    // wave, and so on every SIMD, about equally. A wave runs the step with
+    // only its MA blocks that hold rows: the MFMAs of padding blocks are
+    // skipped (about a quarter of an expert's last tile at the prefill
+    // shape). Every variant loads the same data and meets the same barriers.
+    const int nblk = (tile.rows + 31) / 32;
+    const int nact = nblk >= wm + 9 ? 3 : (nblk >= wm + 5 ? 2 : 1);
+    if (nact == 3)
+      run(IntC<3>{});
+    else if (nact == 2)
+      run(IntC<2>{});
+    else
+      run(IntC<1>{});
 
-    // acc[nb][mb] element i: token row wm*96 + mb*32 + lane%32, weight-tile
+    // acc[nb][mb] element i: token row (wm + 4 mb)*32 + lane%32, weight-tile
     // row (block nb) + 8*(i/4) + 4*(lane/32) + i%4; gate block nb pairs with
     // up block nb + NB/2.
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
-      const int m = wm * 96 + mb * 32 + (lane & 31);
+      const int m = (wm + 4 * mb) * 32 + (lane & 31);
       if (m >= tile.rows) continue;
       const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
 #pragma unroll
