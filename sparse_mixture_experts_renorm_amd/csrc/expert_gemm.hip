@@ -142,10 +142,16 @@ __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets,
   const int te = mt * nN;  // tiles of one split part of expert e
   const int ks = L / te;
   L -= ks * te;
-  const int mi = L % mt;
+  // The expert's rows are cut into its mt row tiles as evenly as 32-row
+  // blocks allow (block counts differ by at most one, each at most BM/32):
+  // the tiles that share a weight tile then take about the same time and
+  // stay in step, and no tile is mostly padding.
+  const int mi = L % mt, nb = (m + 31) / 32;
+  const int b0 = static_cast<int>(static_cast<long long>(mi) * nb / mt);
+  const int b1 = static_cast<int>(static_cast<long long>(mi + 1) * nb / mt);
   res[0] = e;
-  res[1] = offsets[e] + mi * BM;
-  res[2] = m - mi * BM < BM ? m - mi * BM : BM;
+  res[1] = offsets[e] + 32 * b0;
+  res[2] = (32 * b1 < m ? 32 * b1 : m) - 32 * b0;
   res[3] = L / mt;
   res[4] = ks;
 }

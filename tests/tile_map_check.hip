@@ -8,6 +8,7 @@
 #include "../sparse_mixture_experts_renorm_amd/csrc/expert_stream.hip"
 
 #include <cstdio>
+#include <algorithm>
 #include <map>
 #include <random>
 #include <tuple>
@@ -22,6 +23,8 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
                              : tile_grid(rows_bound, E, BM, nN, max_split);
   // key (e, row tile, column tile, part) -> counts {whole, half 0, half 1}
   std::map<std::tuple<int, int, int, int>, std::array<int, 3>> seen;
+  // (e, column tile, part, first row) -> rows
+  std::map<std::tuple<int, int, int, int>, int> rows_of;
   int S = -1;
   std::vector<int> pref(E + 1);
   row_tile_prefix<BM>(off.data(), E, pref.data());
@@ -31,13 +34,45 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
     if (S < 0) S = res[5];
     if (res[5] != S) return printf("split count differs between workgroups\n"), 1;
     if (res[0] < 0) continue;
-    const int e = res[0], m = off[e + 1] - off[e], mi = (res[1] - off[e]) / BM;
-    if (e >= E || res[1] != off[e] + mi * BM || mi < 0 || res[2] != std::min(BM, m - mi * BM) ||
-        res[2] <= 0 || res[3] < 0 || res[3] >= nN || res[4] < 0 || res[4] >= S ||
-        res[6] < -1 || res[6] > 1 || (!TAIL && res[6] != -1))
+    const int e = res[0];
+    if (e >= E || res[1] < off[e] || res[1] % 32 != off[e] % 32 || res[2] <= 0 || res[2] > BM ||
+        res[1] + res[2] > off[e + 1] || res[3] < 0 || res[3] >= nN || res[4] < 0 ||
+        res[4] >= S || res[6] < -1 || res[6] > 1 || (!TAIL && res[6] != -1))
       return printf("bad tile: e %d row0 %d rows %d nt %d ks %d half %d\n", e, res[1], res[2],
                     res[3], res[4], res[6]), 1;
-    seen[{e, mi, res[3], res[4]}][res[6] + 1] += 1;
+    // key by the first row; the rows must cut the expert into its row tiles
+    seen[{e, res[1], res[3], res[4]}][res[6] + 1] += 1;
+    const auto key = std::make_tuple(e, res[3], res[4], res[1]);
+    const auto it = rows_of.find(key);
+    if (it != rows_of.end() && it->second != res[2])
+      return printf("tile at row %d has %d and %d rows\n", res[1], it->second, res[2]), 1;
+    rows_of[key] = res[2];
+  }
+  // per (expert, column tile, part): the row ranges tile [off[e], off[e+1])
+  // exactly, in row tiles that differ by at most 32 rows (before the ragged
+  // end of the last one)
+  {
+    std::map<std::tuple<int, int, int>, std::vector<std::pair<int, int>>> ranges;
+    for (const auto& kv : rows_of)
+      ranges[{std::get<0>(kv.first), std::get<1>(kv.first), std::get<2>(kv.first)}].push_back(
+          {std::get<3>(kv.first), kv.second});
+    for (auto& kv : ranges) {
+      const int e = std::get<0>(kv.first);
+      auto& v = kv.second;
+      std::sort(v.begin(), v.end());
+      int next = off[e], lo = 1 << 30, hi = 0;
+      for (size_t i = 0; i < v.size(); ++i) {
+        if (v[i].first != next) return printf("row tiles of expert %d leave a gap or overlap\n", e), 1;
+        next += v[i].second;
+        const int blocks = (v[i].second + 31) / 32;
+        lo = std::min(lo, blocks);
+        hi = std::max(hi, blocks);
+      }
+      if (next != off[e + 1]) return printf("row tiles of expert %d do not reach its end\n", e), 1;
+      if (hi - lo > 1) return printf("row tiles of expert %d are uneven: %d..%d blocks\n", e, lo, hi), 1;
+      if (static_cast<int>(v.size()) != (off[e + 1] - off[e] + BM - 1) / BM)
+        return printf("expert %d has %zu row tiles\n", e, v.size()), 1;
+    }
   }
   long long expected = 0;
   for (int e = 0; e < E; ++e) expected += static_cast<long long>((off[e + 1] - off[e] + BM - 1) / BM);
@@ -61,7 +96,7 @@ int main() {
   long long tiles = 0;
   int cases = 0;
   const int cus[] = {256, 304, 80, 8, 1};
-  for (int it = 0; it < 3000; ++it) {
+  for (int it = 0; it < 2000; ++it) {
     const int E = 1 + static_cast<int>(rng() % (it % 7 == 0 ? kMaxExperts : 64));
     std::vector<int32_t> off(E + 1, 0);
     for (int e = 0; e < E; ++e) {
