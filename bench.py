@@ -175,6 +175,8 @@ def main():
     names = ["router", "permute", "gate_up", "down", "combine"]
     stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
                 for i, n in enumerate(names)}
+    # the same steps one by one (first to last event of each call)
+    per_step = np.array([evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)])
     cnt = ex["counts"].cpu().numpy()
 
     # ---- roofline of the dominant kernel (gate/up GEMM) ----
@@ -220,6 +222,9 @@ def main():
         "active_tflops": active / layer_s / 1e12,
         "mfma_peak_frac": active / layer_s / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": stage_ms,
+        "step_ms_events": {"median": float(np.median(per_step)), "min": float(per_step.min()),
+                           "max": float(per_step.max()),
+                           "note": "per-call spread from the per-kernel timing loop"},
         "expert_counts": cnt.tolist(),
         "roofline": roof,
         "cpu_baseline": None,

@@ -15,10 +15,12 @@
 // rows. One workgroup of 8 waves per CU (two per SIMD)
 // computes a 256 x 256 tile: 256 permuted rows against 256 weight rows
 // (gate/up: 128 gate rows and the same 128 up rows, giving 128 columns of h;
-// down: 256 columns of y). Each wave owns a 128 x 64 part: 8 accumulators of
-// v_mfma_f32_32x32x16_bf16 (128 fp32 per lane), so each 16-byte fragment read
-// from LDS feeds 2 or 4 MFMAs; with two waves per SIMD one wave's MFMAs run
-// while the other waits for its data. The reduction dimension moves in
+// down: 256 columns of y). Each wave owns 128 token rows (four 32-row blocks,
+// interleaved with the other row group's) against 64 weight rows: 8
+// accumulators of v_mfma_f32_32x32x16_bf16 (128 fp32 per lane), so each
+// 16-byte fragment read from LDS feeds 2 or 4 MFMAs; with two waves per SIMD
+// one wave's MFMAs run while the other waits for its data. A wave skips the
+// MFMAs of its blocks that lie wholly past the tile's rows. The reduction dimension moves in
 // steps of 64 through two LDS stages (64 KB each): the loads of step s+1 go
 // from memory straight to LDS (buffer_load_dwordx4 ... lds, no VGPRs) while
 // the MFMAs of step s run, spread over the first half of the step. Each lane
@@ -38,7 +40,10 @@
 //
 // Tile schedule: the host sizes the grid from an upper bound on the tile
 // count; each workgroup reads the per-expert offsets, counts the real tiles
-// and maps itself to (expert, row tile, column tile). Workgroups are handed
+// and maps itself to (expert, row tile, column tile). An expert's rows are
+// cut into ceil(rows / tile height) row tiles of nearly equal height (whole
+// 32-row blocks), so little of any tile is padding and the row tiles of one
+// weight tile take the same time. Workgroups are handed
 // to the 8 XCDs round-robin, so consecutive tiles of the schedule are given
 // to workgroups on the same XCD (sharing its L2): each XCD takes a
 // contiguous eighth of the tile list. Inside an expert (and split part) the
