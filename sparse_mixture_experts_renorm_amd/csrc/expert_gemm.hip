@@ -59,7 +59,7 @@ namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kMinSplitSteps = 48;
+constexpr int kMinSplitSteps = 12;
 
 struct Tile {
   int e, row0, rows, nt;
