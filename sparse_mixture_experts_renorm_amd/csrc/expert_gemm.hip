@@ -20,10 +20,11 @@
 // accumulators of v_mfma_f32_32x32x16_bf16 (128 fp32 per lane), so each
 // 16-byte fragment read from LDS feeds 2 or 4 MFMAs; with two waves per SIMD
 // one wave's MFMAs run while the other waits for its data. A wave skips the
-// MFMAs of its blocks that lie wholly past the tile's rows. The reduction dimension moves in
-// steps of 64 through two LDS stages (64 KB each): the loads of step s+1 go
-// from memory straight to LDS (buffer_load_dwordx4 ... lds, no VGPRs) while
-// the MFMAs of step s run, spread over the first half of the step. Each lane
+// MFMAs of its blocks that lie wholly past the tile's rows. The reduction
+// dimension moves in steps of 64 through two LDS stages (64 KB each): the
+// loads of step s+1 go from memory straight to LDS (buffer_load_dwordx4 ...
+// lds, no VGPRs) while the MFMAs of step s run, spread over the first half
+// of the step. Each lane
 // supplies its own 32-bit offset, which is how the token gather of the
 // gate/up pass is done; when K is not a multiple of 64, global loads whose
 // lanes past K read a 16-byte zero page are used instead. The step waits
