@@ -146,6 +146,37 @@ def test_expert_ffn_parity(M, T, d, ffn, E, k, dtype, kind):
     assert err <= REL_TOL[dtype] * rms, f"max err {err / rms:.3e} x RMS"
 
 
+# Row counts per expert around the tile heights: the grouped GEMMs cut an
+# expert's rows into ceil(rows / tile height) row tiles of nearly equal height
+# (whole 32-row blocks), and a wave skips the MFMAs of blocks past the tile's
+# rows. k = 1, so each token's output is its one expert's row.
+ROW_SPLITS = [
+    # counts per expert, d, ffn
+    ([769, 1537], 128, 192),                 # tall tiles: 8/8/9 and 9/10/10/10/10 blocks
+    ([384, 385, 1151, 1153], 64, 96),        # tall tiles: exactly one tile, one row more, 3 and 4 tiles
+    ([257, 511, 512, 513, 31, 33], 64, 96),  # 256 x 256 tiles
+    ([1, 32, 33, 800], 64, 96),              # tiny experts beside a large one
+]
+
+
+@pytest.mark.parametrize("counts,d,ffn", ROW_SPLITS)
+def test_expert_ffn_row_splits(M, counts, d, ffn):
+    E, T = len(counts), sum(counts)
+    say(f"moe_expert_ffn row splits counts={counts} d={d} ffn={ffn}")
+    inp = wl.make_custom_inputs(T, d, ffn, E, "bf16", seed=8)
+    idx = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(9).shuffle(idx)
+    idx = idx.reshape(T, 1)
+    w = np.ones((T, 1), dtype=np.float32)
+    args = [dev_tensor(inp[n]) for n in ("w_gate", "w_up", "w_down")]
+    out = M.moe_expert_ffn(dev_tensor(inp["x"]), dev_tensor(idx), dev_tensor(w), *args)
+    torch.cuda.synchronize()
+    ref = O.expert_ffn(inp["x"], idx, w, inp["w_gate"], inp["w_up"], inp["w_down"], E)
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(host(out).astype(np.float64) - ref).max()
+    assert err <= REL_TOL["bf16"] * rms, f"max err {err / rms:.3e} x RMS"
+
+
 # -------------------------------------------------------- whole layer --
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
