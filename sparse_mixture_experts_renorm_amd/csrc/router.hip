@@ -63,12 +63,46 @@ __device__ void route_token(const float* Lrow, int E, int k, float* probs_row,
     v[q] = e < E ? Lrow[e] : -INFINITY;
     key[q] = e < E ? ((static_cast<uint64_t>(order_key(v[q])) << 32) | static_cast<uint32_t>(~e)) : 0ull;
   }
+  int my_e = 0;
+  float my_v = 0.f, v0;
+  if (E <= kWave) {
+    // One key per lane. Lane l's slot is the rank of its key (how many of the
+    // E keys are larger; keys are distinct, so the ranks are 0 .. E-1; lanes
+    // past E hold key 0 and rank E >= k). The keys are read out lane by lane
+    // on the scalar path, then each selected lane hands its expert and logit
+    // to the lane of its slot.
+    const uint32_t khi = static_cast<uint32_t>(key[0] >> 32), klo = static_cast<uint32_t>(key[0]);
+    int rank = 0;
+    for (int m = 0; m < E; ++m) {
+      const uint32_t mhi = __builtin_amdgcn_readlane(khi, m), mlo = __builtin_amdgcn_readlane(klo, m);
+      rank += (mhi > khi || (mhi == khi && mlo > klo)) ? 1 : 0;
+    }
+    my_e = __builtin_amdgcn_ds_permute(rank * 4, lane);
+    my_v = __int_as_float(__builtin_amdgcn_ds_permute(rank * 4, __float_as_int(v[0])));
+    v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+  } else {
+    // k rounds of a 64-lane maximum over four keys per lane
+    v0 = 0.f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
+      best = wave_max_u64(best);
+      const int e = static_cast<int>(~static_cast<uint32_t>(best));
+      const float ve = Lrow[e];
+      if (j == 0) v0 = ve;
+      if (lane == j) { my_e = e; my_v = ve; }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + q * kWave == e) key[q] = 0ull;
+    }
+  }
   if (probs_row) {
-    float m = wave_max_f32(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    // the largest logit is v0, the selected first one
     float z[4], s = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      z[q] = lane + q * kWave < E ? expf(v[q] - m) : 0.f;
+      z[q] = lane + q * kWave < E ? expf(v[q] - v0) : 0.f;
       s += z[q];
     }
     s = wave_sum_f32(s);
@@ -76,21 +110,6 @@ __device__ void route_token(const float* Lrow, int E, int k, float* probs_row,
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (lane + q * kWave < E) probs_row[lane + q * kWave] = z[q] * inv;
-  }
-  int my_e = 0;
-  float my_v = 0.f, v0 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
-    best = wave_max_u64(best);
-    const int e = static_cast<int>(~static_cast<uint32_t>(best));
-    const float ve = Lrow[e];
-    if (j == 0) v0 = ve;
-    if (lane == j) { my_e = e; my_v = ve; }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (lane + q * kWave == e) key[q] = 0ull;
   }
   // renormalised weights over the k selected experts
   const float ex = lane < k ? expf(my_v - v0) : 0.f;
