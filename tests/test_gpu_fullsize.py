@@ -1,9 +1,10 @@
 """Parity at the full workload sizes, in the launch configuration the
 benchmark times (bf16 inputs, fp32 output, one caller workspace).
 
-The oracle evaluates a seeded sample of tokens one by one (tokens are
-independent: no capacity limit), with the same near-tie protocol as the
-small tests. Whole-batch properties are checked exactly: the expert counts
+The layer test evaluates every token with the oracle (a few seconds of
+numpy at these sizes), with the same near-tie protocol as the small tests;
+the block-option and largest-batch tests evaluate seeded samples of tokens
+(tokens are independent: no capacity limit reached). Whole-batch properties are checked exactly: the expert counts
 add up to T*k and match the oracle's counts except where a near-tie token
 moved, and two calls give bit-identical outputs.
 """
@@ -17,8 +18,6 @@ from parity_util import compare_layer, dev_tensor, host, logit_tolerance, routin
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-SAMPLE = {"prefill": 48, "decode": 32, "skewed": 48}
-
 
 @pytest.fixture(scope="module")
 def M():
@@ -30,7 +29,7 @@ def M():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["decode", "prefill", "skewed"])
-def test_fullsize_sampled_parity(M, name):
+def test_fullsize_parity(M, name):
     w = wl.WORKLOADS[name]
     say(f"full-size {name}: T={w.T} d={w.d} ffn={w.ffn} E={w.E} k={w.k}; generating inputs")
     inp = wl.make_layer_inputs(w, seed=0)
@@ -57,13 +56,11 @@ def test_fullsize_sampled_parity(M, name):
     say(f"full-size {name}: counts {counts.tolist()[:16]}..., near-ties {near}, count diff {diff}")
     assert diff <= 2 * near
 
-    rng = np.random.default_rng(1234)
-    tok = np.sort(rng.choice(w.T, size=min(SAMPLE[name], w.T), replace=False))
-    say(f"full-size {name}: oracle on {len(tok)} sampled tokens")
-    st = compare_layer(got[tok], inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
-                       inp["w_down"], w.k, inp["router_bias"], 2e-2, tokens=tok)
+    say(f"full-size {name}: oracle on all {w.T} tokens")
+    st = compare_layer(got, inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                       inp["w_down"], w.k, inp["router_bias"], 2e-2)
     say(f"full-size {name}: max err {st['max_rel_err']:.3e} x RMS (bar 2e-2), "
-        f"sample near-ties {st['near_ties']}")
+        f"near-ties {st['near_ties']}")
 
 
 @pytest.mark.timeout(900)
@@ -92,7 +89,7 @@ def test_fullsize_block_options(M, name):
     cap = O.capacity(w.T, w.E, w.k, 1.25)
     assert routed.max() <= cap and np.array_equal(kept, routed), "an expert reached its capacity"
     rng = np.random.default_rng(99)
-    tok = np.sort(rng.choice(w.T, size=min(SAMPLE[name], w.T), replace=False))
+    tok = np.sort(rng.choice(w.T, size=min(48, w.T), replace=False))
     say(f"full-size block options {name}: oracle on {len(tok)} tokens")
     sub = dict(inp, x=inp["x"][tok])
     ref, _ = O.moe_forward(sub["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
