@@ -177,6 +177,29 @@ def test_expert_ffn_row_splits(M, counts, d, ffn):
     assert err <= REL_TOL["bf16"] * rms, f"max err {err / rms:.3e} x RMS"
 
 
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        E = int(rng.choice([1, 2, 3, 4, 6, 8, 13, 16, 32, 64]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([rng.integers(1, 40), rng.integers(40, 600)]))
+        yield (T, int(16 * rng.integers(1, 17)), int(16 * rng.integers(1, 17)), E, k)
+
+
+@pytest.mark.parametrize("T,d,ffn,E,k", list(_random_shapes(30, 2024)))
+def test_expert_ffn_random_shapes_f32(M, T, d, ffn, E, k):
+    say(f"moe_expert_ffn f32 random shape T={T} d={d} ffn={ffn} E={E} k={k}")
+    inp = wl.make_custom_inputs(T, d, ffn, E, "f32", seed=T + d)
+    idx, w = wl.make_routing(T, E, k, "random", seed=ffn + E)
+    args = [dev_tensor(inp[n]) for n in ("w_gate", "w_up", "w_down")]
+    out = M.moe_expert_ffn(dev_tensor(inp["x"]), dev_tensor(idx), dev_tensor(w), *args)
+    torch.cuda.synchronize()
+    ref = O.expert_ffn(inp["x"], idx, w, inp["w_gate"], inp["w_up"], inp["w_down"], E)
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(host(out).astype(np.float64) - ref).max()
+    assert err <= REL_TOL["f32"] * rms, f"max err {err / rms:.3e} x RMS"
+
+
 # -------------------------------------------------------- whole layer --
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
