@@ -200,6 +200,43 @@ def test_expert_ffn_random_shapes_f32(M, T, d, ffn, E, k):
     assert err <= REL_TOL["f32"] * rms, f"max err {err / rms:.3e} x RMS"
 
 
+def _h_rounding_bound(inp, idx, w, E):
+    """Elementwise bound on what rounding h (the down pass's bf16 operand) to
+    bf16 can move the output: each h element moves by at most 2^-9 of itself,
+    so output (t, c) moves by at most 2^-9 * sum_j w[t,j] * (|h| |W_d|^T)[t, c];
+    the bound takes twice that for the fp32 sums and the SiLU's few ulps."""
+    x = O.widen(inp["x"])
+    out = np.zeros((x.shape[0], inp["w_down"].shape[1]))
+    for e in range(E):
+        tok, slot = np.nonzero(idx == e)
+        if len(tok) == 0:
+            continue
+        g = x[tok] @ O.widen(inp["w_gate"][e]).T
+        u = x[tok] @ O.widen(inp["w_up"][e]).T
+        habs = np.abs(g / (1.0 + np.exp(-g)) * u)
+        out[tok] += w[tok, slot][:, None] * (habs @ np.abs(O.widen(inp["w_down"][e])).T)
+    return 2.0 ** -8 * out
+
+
+@pytest.mark.parametrize("T,d,ffn,E,k", list(_random_shapes(40, 4048)))
+def test_expert_ffn_random_shapes_bf16(M, T, d, ffn, E, k):
+    """Random bf16 shapes, element by element against the oracle within the
+    bound that rounding h to bf16 allows (plus 1e-3 x RMS): short down
+    reductions (few terms per output) can exceed 2e-2 x RMS on rounding
+    alone, so the workloads' bar is not the bar here."""
+    say(f"moe_expert_ffn bf16 random shape T={T} d={d} ffn={ffn} E={E} k={k}")
+    inp = wl.make_custom_inputs(T, d, ffn, E, "bf16", seed=T + d)
+    idx, w = wl.make_routing(T, E, k, "random", seed=ffn + E)
+    args = [dev_tensor(inp[n]) for n in ("w_gate", "w_up", "w_down")]
+    out = M.moe_expert_ffn(dev_tensor(inp["x"]), dev_tensor(idx), dev_tensor(w), *args)
+    torch.cuda.synchronize()
+    ref = O.expert_ffn(inp["x"], idx, w, inp["w_gate"], inp["w_up"], inp["w_down"], E)
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(host(out).astype(np.float64) - ref)
+    bound = _h_rounding_bound(inp, idx, w, E) + 1e-3 * rms
+    assert np.all(err <= bound), f"worst err/bound {np.max(err / bound):.3f}"
+
+
 # -------------------------------------------------------- whole layer --
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
