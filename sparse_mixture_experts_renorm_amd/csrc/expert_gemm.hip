@@ -246,7 +246,7 @@ constexpr int STAGE = TM * TK * 2;  // bytes per operand and stage (32 KB)
 
 // GATE_UP: A = x gathered by sorted_token, weights = [w_gate; w_up], C = h (bf16).
 // !GATE_UP: A = h (rows in order), weights = w_down, C = y (fp32); the
-// reduction may be split (see map_tile): part ks writes C + ks * c_split,
+// reduction may be split (see assign_tile): part ks writes C + ks * c_split,
 // and workgroup 0 stores the split count S in *split_out.
 // NW waves per workgroup: 4 (wave tile 128 x 128, one wave per SIMD) or 8
 // (wave tile 128 x 64, two waves per SIMD, so one wave's MFMAs run while the
@@ -501,7 +501,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 // cost is coarser row padding, so the host takes these tiles only when the
 // experts average at least two tiles' worth of rows. The tiles of an XCD's
 // last, at most half-full round run at half width (384 x 128, 96 x 64 per
-// wave; see map_tile's TAIL). Same swizzle, stages and epilogue as the
+// wave; see assign_tile's TAIL). Same swizzle, stages and epilogue as the
 // 256 x 256 kernel. Which operand and
 // which weight matrix each load instruction serves is fixed per unrolled
 // index, so the compiler keeps the choice in scalar code (chosen at run
@@ -791,7 +791,7 @@ unsigned tile_grid(int rows, int E, int BM, int nN, int splits) {
   return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds);
 }
 
-// tile_grid plus the half-width tail tiles' extra slots (map_tile's TAIL)
+// tile_grid plus the half-width tail tiles' extra slots (assign_tile's TAIL)
 unsigned tall_grid(int rows, int E, int nN, int splits, int n_cu) {
   return tile_grid(rows, E, TM3, nN, splits) + (n_cu / kXcds / 2) * kXcds;
 }
