@@ -101,15 +101,19 @@ moe_status moe_route_logits(const float* logits, int T, int E, int k,
  *   offsets[e+1] = offsets[e] + counts[e]; sorted_token [T*k]: the token of
  *   each permuted row, experts in ascending order and, within an expert,
  *   tokens in ascending order; inv_pos [T*k]: the row of assignment t*k+j.
+ *   topk_w [T, k] fp32 and sorted_w [T*k] fp32: both NULL, or both given,
+ *   then sorted_w[inv_pos[i]] = topk_w[i] (the gate weights in permuted
+ *   order, copied bit for bit); one without the other is INVALID_ARG.
  * All integer; bit-exact. Source: axonml-nn MoELayer::forward (utilisation
  * counts; per-expert token lists gathered in token order).
  * ws: caller scratch of moe_permute_workspace_size(T, E, k) bytes (per-block
  * expert histograms when T*k is large; the size is 0, and ws may be NULL,
  * when one workgroup does the whole job). WORKSPACE_TOO_SMALL below it. */
 size_t moe_permute_workspace_size(int T, int E, int k);
-moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k,
+moe_status moe_permute(const int32_t* topk_idx, const float* topk_w, int T, int E, int k,
                        int32_t* counts, int32_t* offsets, int32_t* sorted_token,
-                       int32_t* inv_pos, void* ws, size_t ws_bytes, hipStream_t stream);
+                       int32_t* inv_pos, float* sorted_w, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* The expert half of the layer for a given routing: permute, per-expert
  * SwiGLU h = SiLU(X W_g^T) * (X W_u^T), y = h W_d^T, and the weighted combine

@@ -53,7 +53,7 @@ def lib() -> ctypes.CDLL:
         _p("moe_route", i, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp)
         _p("moe_route_logits", i, vp, i, i, i, vp, vp, vp, vp)
         _p("moe_permute_workspace_size", sz, i, i, i)
-        _p("moe_permute", i, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp)
+        _p("moe_permute", i, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp)
         _p("moe_expert_ffn", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, sz, vp)
         _p("moe_forward", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp, vp, sz, vp)
         _p("moe_forward_profiled", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp,
@@ -158,22 +158,28 @@ def moe_route(x, w_router, k, router_bias=None, want_logits=False, want_probs=Fa
     return out
 
 
-def moe_permute(topk_idx, E, stream=None):
-    """Returns (counts [E], offsets [E+1], sorted_token [T*k], inv_pos [T*k]), all int32."""
-    _dev(topk_idx)
+def moe_permute(topk_idx, E, topk_w=None, stream=None):
+    """Returns (counts [E], offsets [E+1], sorted_token [T*k], inv_pos [T*k]), all
+    int32, and with topk_w (f32 [T,k]) also sorted_w (f32 [T*k]), the weights in
+    permuted order."""
+    _dev(topk_idx, topk_w)
     assert topk_idx.dtype == torch.int32 and topk_idx.dim() == 2
     T, k = topk_idx.shape
+    if topk_w is not None:
+        assert topk_w.dtype == torch.float32 and tuple(topk_w.shape) == (T, k)
     dev = topk_idx.device
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     st = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sw = torch.empty(T * k, dtype=torch.float32, device=dev) if topk_w is not None else None
     n = int(lib().moe_permute_workspace_size(T, E, k))
     ws = torch.empty(n + 256, dtype=torch.uint8, device=dev) if n else None
     wp, wn = _ws_ptr(ws) if n else (None, 0)
-    _check(lib().moe_permute(_ptr(topk_idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(st),
-                             _ptr(inv), wp, wn, _stream(stream)), "moe_permute")
-    return counts, offsets, st, inv
+    _check(lib().moe_permute(_ptr(topk_idx), _ptr(topk_w), T, E, k, _ptr(counts), _ptr(offsets),
+                             _ptr(st), _ptr(inv), _ptr(sw), wp, wn, _stream(stream)),
+           "moe_permute")
+    return (counts, offsets, st, inv) if sw is None else (counts, offsets, st, inv, sw)
 
 
 def moe_router_stats(probs, counts, stream=None):

@@ -145,6 +145,8 @@ int permute_blocks(int T, int k);
 moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int cap, int32_t* counts,
                           int32_t* routed_counts, int32_t* offsets, int32_t* sorted_token,
                           int32_t* inv_pos, int32_t* block_counts, hipStream_t s);
+moe_status launch_permute_weights(const int32_t* inv_pos, const float* topk_w, int n,
+                                  float* sorted_w, hipStream_t s);
 // S shared experts over all T tokens: rows s*T + t hold token t.
 moe_status launch_identity_rows(int T, int S, int32_t* sorted_token, int32_t* offsets,
                                 hipStream_t s);

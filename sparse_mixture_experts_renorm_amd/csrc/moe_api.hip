@@ -119,20 +119,23 @@ size_t moe_permute_workspace_size(int T, int E, int k) {
   return static_cast<size_t>(permute_blocks(T, k)) * E * sizeof(int32_t);
 }
 
-moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
-                       int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+moe_status moe_permute(const int32_t* topk_idx, const float* topk_w, int T, int E, int k,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* inv_pos,
+                       float* sorted_w, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_routing(T, E, k);
   if (st != MOE_OK) return st;
+  if ((topk_w == nullptr) != (sorted_w == nullptr)) return MOE_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(topk_idx) || !ok_ptr(counts) || !ok_ptr(offsets) || !ok_ptr(sorted_token) ||
-      !ok_ptr(inv_pos))
+      !ok_ptr(inv_pos) || !ok_opt(topk_w) || !ok_opt(sorted_w))
     return MOE_INVALID_ARG;
   const size_t need = moe_permute_workspace_size(T, E, k);
   if (need > 0 && !ok_ptr(ws)) return MOE_INVALID_ARG;
   if (ws_bytes < need) return MOE_WORKSPACE_TOO_SMALL;
-  return launch_permute(topk_idx, T, E, k, T, counts, nullptr, offsets, sorted_token, inv_pos,
-                        static_cast<int32_t*>(ws), stream);
+  st = launch_permute(topk_idx, T, E, k, T, counts, nullptr, offsets, sorted_token, inv_pos,
+                      static_cast<int32_t*>(ws), stream);
+  if (st != MOE_OK || !sorted_w) return st;
+  return launch_permute_weights(inv_pos, topk_w, T * k, sorted_w, stream);
 }
 
 size_t moe_router_stats_workspace_size(int T, int E) {

@@ -228,6 +228,17 @@ moe_status launch_permute(const int32_t* topk_idx, int T, int E, int k, int cap,
 }
 
 namespace {
+// The gate weights in permuted order: sorted_w[inv_pos[i]] = topk_w[i]
+// (skipping dropped assignments, inv_pos = -1).
+__global__ __launch_bounds__(256) void permute_weights_kernel(const int32_t* __restrict__ inv_pos,
+                                                              const float* __restrict__ topk_w,
+                                                              int n, float* __restrict__ sorted_w) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int p = inv_pos[i];
+  if (p >= 0) sorted_w[p] = topk_w[i];
+}
+
 // Shared experts take every token: expert s owns rows s*T .. s*T + T-1,
 // row s*T + t holding token t.
 __global__ __launch_bounds__(256) void identity_rows_kernel(int T, int S, int32_t* sorted_token,
@@ -237,6 +248,12 @@ __global__ __launch_bounds__(256) void identity_rows_kernel(int T, int S, int32_
   if (i <= static_cast<size_t>(S)) offsets[i] = static_cast<int32_t>(i * T);
 }
 }  // namespace
+
+moe_status launch_permute_weights(const int32_t* inv_pos, const float* topk_w, int n,
+                                  float* sorted_w, hipStream_t s) {
+  permute_weights_kernel<<<(n + 255) / 256, 256, 0, s>>>(inv_pos, topk_w, n, sorted_w);
+  return launch_status();
+}
 
 moe_status launch_identity_rows(int T, int S, int32_t* sorted_token, int32_t* offsets,
                                 hipStream_t s) {

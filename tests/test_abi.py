@@ -95,17 +95,22 @@ def test_forward_validation(L):
 
 def test_expert_ffn_and_permute_validation(L):
     p = ctypes.c_void_p(256)
+    bad = ctypes.c_void_p(260)  # not 16-byte aligned
     assert L.moe_expert_ffn(p, p, p, p, p, p, 8, 64, 64, 4, 5, BF16, p, F32, p, 1 << 30, None) == INVALID
     assert L.moe_expert_ffn(p, p, p, p, p, p, 8, 64, 64, 4, 2, BF16, p, F32, p, 10, None) == WS_SMALL
-    assert L.moe_permute(p, 8, 4, 5, p, p, p, p, None, 0, None) == INVALID
-    assert L.moe_permute(p, 8, 257, 2, p, p, p, p, None, 0, None) == UNSUPPORTED
-    assert L.moe_permute(None, 8, 4, 2, p, p, p, p, None, 0, None) == INVALID
+    assert L.moe_permute(p, None, 8, 4, 5, p, p, p, p, None, None, 0, None) == INVALID
+    assert L.moe_permute(p, None, 8, 257, 2, p, p, p, p, None, None, 0, None) == UNSUPPORTED
+    assert L.moe_permute(None, None, 8, 4, 2, p, p, p, p, None, None, 0, None) == INVALID
+    # the weights and their permuted copy come together or not at all
+    assert L.moe_permute(p, p, 8, 4, 2, p, p, p, p, None, None, 0, None) == INVALID
+    assert L.moe_permute(p, None, 8, 4, 2, p, p, p, p, p, None, 0, None) == INVALID
+    assert L.moe_permute(p, p, 8, 4, 2, p, p, p, p, bad, None, 0, None) == INVALID
     # one workgroup up to 4096 assignments (no scratch), then per-block histograms
     assert L.moe_permute_workspace_size(2048, 8, 2) == 0
     assert L.moe_permute_workspace_size(8192, 64, 8) == 64 * 64 * 4
     assert L.moe_permute_workspace_size(1 << 20, 8, 2) == 256 * 8 * 4
-    assert L.moe_permute(p, 8192, 64, 8, p, p, p, p, None, 0, None) == INVALID
-    assert L.moe_permute(p, 8192, 64, 8, p, p, p, p, p, 64 * 64 * 4 - 1, None) == WS_SMALL
+    assert L.moe_permute(p, None, 8192, 64, 8, p, p, p, p, None, None, 0, None) == INVALID
+    assert L.moe_permute(p, None, 8192, 64, 8, p, p, p, p, None, p, 64 * 64 * 4 - 1, None) == WS_SMALL
     assert L.moe_route(p, p, None, 8, 40, 4, 2, BF16, None, None, p, p, None) == UNSUPPORTED
     ev = (ctypes.c_void_p * 6)(*([16] * 5 + [0]))
     assert L.moe_forward_profiled(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, p, F32, None, None,

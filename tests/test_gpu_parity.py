@@ -57,14 +57,18 @@ def test_permute_bitexact(M, kind, T, E, k):
     if kind == "one_heavy" and E < 2 and k > 1:
         pytest.skip("needs E >= 2")
     say(f"moe_permute kind={kind} T={T} E={E} k={k}")
-    idx, _ = wl.make_routing(T, E, k, kind, seed=T)
-    counts, offsets, st, inv = M.moe_permute(dev_tensor(idx), E)
+    idx, w = wl.make_routing(T, E, k, kind, seed=T)
+    counts, offsets, st, inv, sw = M.moe_permute(dev_tensor(idx), E, topk_w=dev_tensor(w))
     torch.cuda.synchronize()
     c_ref, o_ref, st_ref, inv_ref = O.permute(idx, E)
     assert np.array_equal(host(counts), c_ref)
     assert np.array_equal(host(offsets), o_ref)
     assert np.array_equal(host(st), st_ref)
     assert np.array_equal(host(inv), inv_ref)
+    # the weights in permuted order, bit for bit: row inv_ref[i] holds w[i]
+    sw_ref = np.empty(T * k, np.float32)
+    sw_ref[inv_ref] = w.reshape(-1)
+    assert np.array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
