@@ -32,9 +32,11 @@
  *   - Non-finite inputs are outside the contract (the page's sort cannot
  *     order NaN); they are not detected on the device.
  *   - Limits (MOE_UNSUPPORTED beyond them): E <= 256, k <= 16,
- *     d % 16 == 0, ffn % 16 == 0, T * k < 2^31, and in bytes of the storage
- *     dtype T*d, T*k*ffn and ffn*d below 2^32 (the GEMM kernels address x,
- *     the hidden activations and one expert's weights with 32-bit offsets).
+ *     d % 16 == 0, ffn % 16 == 0, T * k < 2^31 - 2^20 (the permutation's
+ *     per-block ranges of assignments are 32-bit), and in bytes of the
+ *     storage dtype T*d, T*k*ffn and ffn*d below 2^32 (the GEMM kernels
+ *     address x, the hidden activations and one expert's weights with 32-bit
+ *     offsets).
  *   - Results are deterministic: no floating-point atomics are used, so two
  *     calls on the same inputs give bit-identical outputs.
  */
@@ -202,8 +204,10 @@ moe_status moe_router_stats(const float* probs, const int32_t* counts, int T, in
  * Workspace: moe_forward_ext_workspace_size(...) bytes, 256-byte aligned.
  * Errors as moe_forward, plus INVALID_ARG for opt == NULL, a negative or
  * non-finite capacity factor, norm_eps <= 0, n_shared < 0, shared_ffn < 1
- * or a null or misaligned shared weight; UNSUPPORTED for n_shared > 16 or
- * shared_ffn % 16 != 0. */
+ * or a null or misaligned shared weight; UNSUPPORTED for n_shared > 16,
+ * shared_ffn % 16 != 0, or shared_ffn * d or T * n_shared * shared_ffn
+ * elements of dt reaching 2^32 bytes (32-bit offsets, as for the routed
+ * experts). */
 typedef struct {
   float capacity_factor;
   const void* norm_weight;

@@ -14,6 +14,7 @@ constexpr int kMaxTopK = 16;      // library limit on k
 constexpr int kMaxDownSplit = 4;  // most parts the down GEMM's reduction is cut into
 constexpr int kPermMaxBlocks = 256;            // most workgroups of the permutation
 constexpr long long kPermBlockedFrom = 4096;   // up to this many assignments: one workgroup
+constexpr long long kMaxAssignments = (1ll << 31) - (1ll << 20);  // T*k must stay below
 
 typedef uint16_t bf16_t;          // bfloat16 storage (bit pattern)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

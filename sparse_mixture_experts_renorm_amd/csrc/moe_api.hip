@@ -19,7 +19,9 @@ bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
 moe_status check_routing(int T, int E, int k) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_INVALID_ARG;
   if (E > kMaxExperts || k > kMaxTopK) return MOE_UNSUPPORTED;
-  if (static_cast<long long>(T) * k >= (1ll << 31)) return MOE_UNSUPPORTED;
+  // the permutation's per-block assignment ranges are int32: with 256 blocks
+  // they reach T*k + 2^18, so 2^20 of headroom keeps them below 2^31
+  if (static_cast<long long>(T) * k >= kMaxAssignments) return MOE_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -41,8 +43,8 @@ moe_status check_layer(int T, int d, int ffn, int E, int k, moe_dtype dt) {
 
 bool ok_dtype(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 
-// Options of the extended forward; T only bounds the shared experts' rows.
-moe_status check_options(const moe_options* o, int T, moe_dtype dt) {
+// Options of the extended forward; T and d bound the shared experts' sizes.
+moe_status check_options(const moe_options* o, int T, int d, moe_dtype dt) {
   if (!o) return MOE_INVALID_ARG;
   if (!(o->capacity_factor >= 0.f) || !std::isfinite(o->capacity_factor)) return MOE_INVALID_ARG;
   if (o->norm_weight && (!aligned16(o->norm_weight) || !(o->norm_eps > 0.f) ||
@@ -56,7 +58,10 @@ moe_status check_options(const moe_options* o, int T, moe_dtype dt) {
     if (o->n_shared > kMaxShared || o->shared_ffn % 16 != 0) return MOE_UNSUPPORTED;
     if (static_cast<long long>(T) * o->n_shared >= (1ll << 31)) return MOE_UNSUPPORTED;
     const long long es = dt == MOE_BF16 ? 2 : 4;
-    if (static_cast<long long>(T) * o->n_shared * o->shared_ffn * es >= (1ll << 32))
+    // h_s rows and one shared expert's weights use 32-bit byte offsets in
+    // the tiled GEMMs, as the routed experts' do
+    if (static_cast<long long>(T) * o->n_shared * o->shared_ffn * es >= (1ll << 32) ||
+        static_cast<long long>(o->shared_ffn) * d * es >= (1ll << 32))
       return MOE_UNSUPPORTED;
   }
   return MOE_OK;
@@ -196,20 +201,33 @@ moe_status moe_expert_ffn(const void* x, const int32_t* topk_idx, const float* t
                      w, nullptr, stream, nullptr);
 }
 
-static moe_status forward_impl(const void* x, const void* w_router, const void* w_gate,
-                               const void* w_up, const void* w_down, const float* router_bias,
-                               int T, int d, int ffn, int E, int k, moe_dtype dt, void* out,
-                               moe_dtype out_dt, float* logits_out, float* probs_out,
-                               int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                               hipEvent_t* ev) {
+// Argument checks of moe_forward apart from the workspace.
+static moe_status check_forward(const void* x, const void* w_router, const void* w_gate,
+                                const void* w_up, const void* w_down, const float* router_bias,
+                                int T, int d, int ffn, int E, int k, moe_dtype dt, void* out,
+                                moe_dtype out_dt, float* logits_out, float* probs_out,
+                                int32_t* counts_out) {
   moe_status st = check_layer(T, d, ffn, E, k, dt);
   if (st != MOE_OK) return st;
   if (!ok_dtype(out_dt)) return MOE_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(w_router) || !ok_ptr(w_gate) || !ok_ptr(w_up) || !ok_ptr(w_down) ||
       !ok_ptr(out) || !ok_opt(router_bias) || !ok_opt(logits_out) || !ok_opt(probs_out) ||
-      !ok_opt(counts_out) || !ok_ptr(ws) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+      !ok_opt(counts_out))
     return MOE_INVALID_ARG;
+  return MOE_OK;
+}
+
+static moe_status forward_impl(const void* x, const void* w_router, const void* w_gate,
+                               const void* w_up, const void* w_down, const float* router_bias,
+                               int T, int d, int ffn, int E, int k, moe_dtype dt, void* out,
+                               moe_dtype out_dt, float* logits_out, float* probs_out,
+                               int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                               hipEvent_t* ev) {
+  moe_status st = check_forward(x, w_router, w_gate, w_up, w_down, router_bias, T, d, ffn, E, k,
+                                dt, out, out_dt, logits_out, probs_out, counts_out);
+  if (st != MOE_OK || T == 0) return st;
+  if (!ok_ptr(ws) || (reinterpret_cast<uintptr_t>(ws) & 255u)) return MOE_INVALID_ARG;
   const Workspace w = carve_workspace(ws, T, d, ffn, E, k, dt);
   if (ws_bytes < w.bytes) return MOE_WORKSPACE_TOO_SMALL;
   if (ev) hipEventRecord(ev[0], stream);
@@ -246,7 +264,7 @@ moe_status moe_forward_profiled(const void* x, const void* w_router, const void*
 
 size_t moe_forward_ext_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt,
                                       const moe_options* opt) {
-  if (check_layer(T, d, ffn, E, k, dt) != MOE_OK || check_options(opt, T, dt) != MOE_OK) return 0;
+  if (check_layer(T, d, ffn, E, k, dt) != MOE_OK || check_options(opt, T, d, dt) != MOE_OK) return 0;
   return carve_ext_workspace(nullptr, T, d, ffn, E, k, dt, opt->norm_weight != nullptr,
                              opt->n_shared, opt->shared_ffn)
       .bytes;
@@ -260,7 +278,7 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
                            size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_layer(T, d, ffn, E, k, dt);
   if (st != MOE_OK) return st;
-  st = check_options(opt, T, dt);
+  st = check_options(opt, T, d, dt);
   if (st != MOE_OK) return st;
   if (!ok_dtype(out_dt)) return MOE_UNSUPPORTED;
   if (T == 0) return MOE_OK;

@@ -119,6 +119,23 @@ def test_expert_ffn_and_permute_validation(L):
                                   None, p, 1 << 30, None, None) == INVALID
 
 
+def test_assignment_limit(L):
+    """T*k stays below 2^31 - 2^20: the permutation's per-block assignment
+    ranges run up to T*k + 2^18 in int32. At the limit every routing entry
+    point rejects the call; just below it the checks pass (the permutation
+    then stops at its workspace check, before any device work)."""
+    p = ctypes.c_void_p(256)
+    lim = (1 << 31) - (1 << 20)
+    k = 2
+    T_over, T_under = lim // k, lim // k - 1
+    assert L.moe_permute(p, None, T_over, 8, k, p, p, p, p, None, p, 0, None) == UNSUPPORTED
+    assert L.moe_permute(p, None, T_under, 8, k, p, p, p, p, None, p, 0, None) == WS_SMALL
+    assert L.moe_permute_workspace_size(T_over, 8, k) == 0
+    assert L.moe_permute_workspace_size(T_under, 8, k) == 256 * 8 * 4
+    assert L.moe_route_logits(p, T_over, 8, k, None, p, p, None) == UNSUPPORTED
+    assert L.moe_route(p, p, None, T_over, 64, 8, k, BF16, None, None, p, p, None) == UNSUPPORTED
+
+
 def test_router_stats_validation(L):
     p = ctypes.c_void_p(256)
     n = L.moe_router_stats_workspace_size(1000, 8)
@@ -188,6 +205,19 @@ def test_forward_ext_validation(L):
     o.shared_down = None
     assert call() == INVALID
     o.shared_down = 256
+    # one shared expert's weights are addressed with 32-bit byte offsets, as
+    # the routed experts' are: shared_ffn * d * 2 bytes must stay below 2^32
+    o.n_shared = 1
+    o.shared_ffn = (1 << 32) // (4096 * 2)
+    def call_d(T=1, ws_bytes=0):
+        return L.moe_forward_ext(p, p, p, p, p, None, T, 4096, 64, 4, 2, BF16, ctypes.byref(o), p,
+                                 F32, None, None, None, None, p, ws_bytes, None)
+    assert call_d() == UNSUPPORTED
+    assert L.moe_forward_ext_workspace_size(1, 4096, 64, 4, 2, BF16, ctypes.byref(o)) == 0
+    o.shared_ffn -= 16
+    assert call_d() == WS_SMALL
+    o.n_shared = 2
+    o.shared_ffn = 64
     need = L.moe_forward_ext_workspace_size(16, 64, 64, 4, 2, BF16, ctypes.byref(o))
     assert need > L.moe_workspace_size(16, 64, 64, 4, 2, BF16)
     assert call(ws_bytes=need - 1) == WS_SMALL
