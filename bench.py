@@ -20,7 +20,12 @@ Prints one JSON line: tokens/s for the layer, plus
                   with each block option (capacity factor 1.25; RMSNorm and
                   residual; one shared expert of the routed experts' width;
                   all together), each as a whole-layer step against the
-                  layer's bound (active FLOPs, or bytes for decode).
+                  layer's bound (active FLOPs, or bytes for decode); and,
+                  under extras.workloads, the decode, small and skewed
+                  configurations of the layer, each measured like the
+                  headline (ms/step, tokens/s, stage times, the gate/up
+                  kernel's roofline, the layer's fraction of the bf16 peak or,
+                  for decode, of HBM bandwidth over its algorithmic bytes).
 """
 import argparse
 import json
@@ -100,6 +105,9 @@ def main():
                     help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router-statistics and block-option timings")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="with the prefill workload, skip the decode, small and skewed "
+                         "measurements reported under extras.workloads")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timing of the layer call replayed from a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -146,61 +154,13 @@ def main():
     dv = {n: to_dev(v) for n, v in inp.items()}
     out = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
     ws = moe.workspace(w.T, w.d, w.ffn, w.E, w.k, dv["x"].dtype, dev)
-    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
     call = dict(router_bias=dv["router_bias"], out=out, ws=ws)
     lay = (dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k)
 
-    log(f"warmup x{args.warmup}")
-    for _ in range(args.warmup):
-        moe.moe_forward(*lay, **call)
-    torch.cuda.synchronize()
-
-    # ---- timed region: K whole-layer steps, events around the loop ----
-    log(f"timed x{args.steps}")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        moe.moe_forward(*lay, **call)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-
-    # ---- per-kernel times: events between the layer's kernels, same stream ----
-    log(f"per-kernel timing x{args.steps}")
-    evs = [moe.stage_events() for _ in range(args.steps)]
-    for s in range(args.steps):
-        _, ex = moe.moe_forward(*lay, **call, want_counts=True, stage_events=evs[s])
-    torch.cuda.synchronize()
-    names = ["router", "permute", "gate_up", "down", "combine"]
-    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-                for i, n in enumerate(names)}
-    # the same steps one by one (first to last event of each call)
-    per_step = np.array([evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)])
-    cnt = ex["counts"].cpu().numpy()
-
-    # ---- roofline of the dominant kernel (gate/up GEMM) ----
-    rows = w.T * w.k
-    touched = int(np.count_nonzero(cnt))
-    gu_flops = 4.0 * rows * w.d * w.ffn
-    gu_bytes = touched * 2 * w.ffn * w.d * 2 + rows * w.d * 2 + rows * w.ffn * 2
-    gu_s = stage_ms["gate_up"] / 1e3
-    if rows > 32 * w.E:   # tiled MFMA kernels (the library's own switches)
-        kern = "expert_gemm_bf16_kernel"
-        kmask = "true" if w.d % 64 else "false"
-        kname = (f"expert_gemm_tall_kernel<true, {kmask}>" if rows >= 2 * 384 * w.E
-                 else f"expert_gemm_bf16_kernel<true, 8, {kmask}>")
-        roof = {"kernel": kname, "bound": "mfma",
-                "achieved": gu_flops / gu_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:                   # weight-streaming kernels
-        kern = "expert_stream_kernel"
-        nb = 1 if rows <= 16 * w.E else 2
-        roof = {"kernel": f"expert_stream_kernel<true, 1, {nb}>", "bound": "hbm",
-                "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["mean_ms"] = stage_ms["gate_up"]
-    roof["algorithmic_per_launch"] = gu_flops if roof["bound"] == "mfma" else gu_bytes
-    roof["traffic"] = measured_traffic(w.name, kern)
+    m = measure_layer(moe, w, dv, args.steps, args.warmup)
+    ms_per_step = m["ms_per_step"]
+    roof = m["roofline"]
+    roof["traffic"] = measured_traffic(w.name, roof.pop("kernel_family"))
 
     active = w.active_flops
     layer_s = ms_per_step / 1e3
@@ -221,14 +181,14 @@ def main():
                    "out_dtype": "f32", "router_bias": w.zipf_bias},
         "active_tflops": active / layer_s / 1e12,
         "mfma_peak_frac": active / layer_s / 1e12 / PEAK_BF16_TFLOPS,
-        "stages_ms": stage_ms,
-        "step_ms_events": {"median": float(np.median(per_step)), "min": float(per_step.min()),
-                           "max": float(per_step.max()),
-                           "note": "per-call spread from the per-kernel timing loop"},
-        "expert_counts": cnt.tolist(),
+        "stages_ms": m["stages_ms"],
+        "step_ms_events": m["step_ms_events"],
+        "expert_counts": m["expert_counts"],
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if "layer_hbm_frac" in m:
+        result["layer_hbm_frac"] = m["layer_hbm_frac"]
 
     if not args.no_graph:
         # the same call captured once into a HIP graph and replayed: the
@@ -250,6 +210,8 @@ def main():
 
     if not args.no_extras:
         result["extras"] = extras(args, w, moe, wl, dv, lay, call, to_dev, log)
+    if not args.no_workloads and w.name == "prefill":
+        result.setdefault("extras", {})["workloads"] = other_workloads(args, moe, wl, dv, to_dev, log)
 
     if not args.no_cpu_baseline:
         from oracle import moe_oracle as O
@@ -269,6 +231,125 @@ def main():
             "sample": f"first {S} of the {w.T} tokens of the same seeded workload, fp64 numpy "
                       f"oracle, all experts' weights widened, {dt:.1f}s"}
     print(json.dumps(result), flush=True)
+
+
+def gate_up_kernel(w, rows):
+    """Name and family of the gate/up kernel the library launches for this
+    shape (its own switches: weight streaming for at most 32 rows per expert
+    on average, 384-row tiles from 768, 256-row tiles between)."""
+    kmask = "true" if w.d % 64 else "false"
+    if rows <= 32 * w.E:
+        nb = 1 if rows <= 16 * w.E else 2
+        return f"expert_stream_kernel<true, 1, {nb}>", "expert_stream_kernel", "hbm"
+    if rows >= 2 * 384 * w.E:
+        return f"expert_gemm_tall_kernel<true, {kmask}>", "expert_gemm_bf16_kernel", "mfma"
+    return f"expert_gemm_bf16_kernel<true, 8, {kmask}>", "expert_gemm_bf16_kernel", "mfma"
+
+
+def measure_layer(moe, w, dv, steps, warmup):
+    """Time moe_forward on resident inputs: `warmup` untimed calls, `steps`
+    timed calls between two events, then `steps` calls of
+    moe_forward_profiled whose events (recorded on the layer's stream between
+    its kernels) give each stage's time. Returns the figures of one workload:
+    ms per step, stage times, expert counts and the roofline of the gate/up
+    kernel (algorithmic FLOPs, or bytes when it streams weights, over its
+    mean event-timed duration)."""
+    import numpy as np
+    import torch
+    dev = dv["x"].device
+    out = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+    ws = moe.workspace(w.T, w.d, w.ffn, w.E, w.k, dv["x"].dtype, dev)
+    call = dict(router_bias=dv["router_bias"], out=out, ws=ws)
+    lay = (dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], w.k)
+    log(f"{w.name}: warmup x{warmup}")
+    for _ in range(warmup):
+        moe.moe_forward(*lay, **call)
+    torch.cuda.synchronize()
+    # ---- timed region: `steps` whole-layer steps, events around the loop ----
+    log(f"{w.name}: timed x{steps}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        moe.moe_forward(*lay, **call)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    # ---- per-kernel times: events between the layer's kernels, same stream ----
+    log(f"{w.name}: per-kernel timing x{steps}")
+    evs = [moe.stage_events() for _ in range(steps)]
+    for s in range(steps):
+        _, ex = moe.moe_forward(*lay, **call, want_counts=True, stage_events=evs[s])
+    torch.cuda.synchronize()
+    names = ["router", "permute", "gate_up", "down", "combine"]
+    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]))
+                for i, n in enumerate(names)}
+    per_step = np.array([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)])
+    cnt = ex["counts"].cpu().numpy()
+
+    rows = w.T * w.k
+    touched = int(np.count_nonzero(cnt))
+    es = 2 if w.dtype == "bf16" else 4
+    gu_flops = 4.0 * rows * w.d * w.ffn
+    gu_bytes = touched * 2 * w.ffn * w.d * es + rows * w.d * es + rows * w.ffn * es
+    gu_s = stage_ms["gate_up"] / 1e3
+    kname, family, bound = gate_up_kernel(w, rows)
+    if bound == "mfma":
+        roof = {"kernel": kname, "bound": "mfma", "achieved": gu_flops / gu_s / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": kname, "bound": "hbm", "achieved": gu_bytes / gu_s / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["mean_ms"] = stage_ms["gate_up"]
+    roof["algorithmic_per_launch"] = gu_flops if bound == "mfma" else gu_bytes
+    roof["kernel_family"] = family
+    layer_s = ms_per_step / 1e3
+    res = {"ms_per_step": ms_per_step, "tokens/s": w.T / layer_s,
+           "active_tflops": w.active_flops / layer_s / 1e12,
+           "mfma_peak_frac": w.active_flops / layer_s / 1e12 / PEAK_BF16_TFLOPS,
+           "stages_ms": stage_ms,
+           "stage_tflops": {"gate_up": gu_flops / gu_s / 1e12,
+                            "down": 2.0 * rows * w.d * w.ffn / (stage_ms["down"] / 1e3) / 1e12},
+           "step_ms_events": {"median": float(np.median(per_step)), "min": float(per_step.min()),
+                              "max": float(per_step.max()),
+                              "note": "per-call spread from the per-kernel timing loop"},
+           "expert_counts": cnt.tolist(), "roofline": roof}
+    if bound == "hbm":
+        # the layer's algorithmic bytes: every touched expert's three weight
+        # matrices, the router weights, x read and out written (fp32)
+        layer_bytes = touched * 3.0 * w.d * w.ffn * es + w.E * w.d * es + w.T * w.d * (es + 4)
+        res["layer_bytes"] = layer_bytes
+        res["layer_hbm_GB/s"] = layer_bytes / layer_s / 1e9
+        res["layer_hbm_frac"] = layer_bytes / layer_s / 1e9 / PEAK_HBM_GBS
+    return res
+
+
+def other_workloads(args, moe, wl, dv, to_dev, log):
+    """The other configurations of the layer, each timed like the headline
+    (warmup, then `steps` timed whole-layer calls and `steps` profiled ones):
+    decode (its 32 tokens are the first rows of the prefill draw and its
+    weights the prefill weights, so the resident tensors are reused), small
+    and skewed (drawn here)."""
+    res = {}
+    dec = wl.WORKLOADS["decode"]
+    ddv = dict(dv, x=dv["x"][:dec.T].contiguous())
+    r = measure_layer(moe, dec, ddv, args.steps, args.warmup)
+    r["roofline"].pop("kernel_family")
+    res["decode"] = r
+    log(f"decode: {r['ms_per_step']:.3f} ms/step, layer {r.get('layer_hbm_frac', 0):.3f} of HBM")
+    for name in ("small", "skewed"):
+        w = wl.WORKLOADS[name]
+        log(f"{name}: generating seeded inputs")
+        inp = wl.make_layer_inputs(w, seed=0)
+        wdv = {n: to_dev(v) for n, v in inp.items()}
+        del inp
+        r = measure_layer(moe, w, wdv, args.steps, args.warmup)
+        r["roofline"].pop("kernel_family")
+        res[name] = r
+        log(f"{name}: {r['ms_per_step']:.3f} ms/step, {r['mfma_peak_frac']:.3f} of bf16 peak")
+        del wdv
+    return res
 
 
 def _timed(fn, steps, warmup):
