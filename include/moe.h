@@ -156,6 +156,31 @@ moe_status moe_forward_profiled(const void* x, const void* w_router, const void*
                                 void* ws, size_t ws_bytes, hipStream_t stream,
                                 hipEvent_t* stage_events);
 
+/* ---- The layer without a workspace argument -----------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * computation, outputs and argument rules as moe_forward, but the workspace
+ * is a fixed array of MOE_NO_ALLOC_SCRATCH_BYTES in the library's own device
+ * memory (one copy per GPU the library runs on, held until the process
+ * ends). The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library routine. The caller still passes inputs and outputs.
+ * Limit: shapes whose moe_workspace_size(T, d, ffn, E, k, dt) exceeds
+ * MOE_NO_ALLOC_SCRATCH_BYTES return MOE_WORKSPACE_TOO_SMALL and enqueue
+ * nothing (at the Mixtral widths d = 4096, ffn = 14336, E = 8, k = 2 that
+ * is T above 356 tokens: decode-sized batches fit). The first call on a
+ * device looks up that device's copy of the array (MOE_HIP_ERROR if the
+ * lookup fails). Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and give undefined
+ * results; calls in order on one stream are safe. No state is carried from
+ * one call to the next. */
+#define MOE_NO_ALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_no_alloc(const void* x, const void* w_router, const void* w_gate,
+                                const void* w_up, const void* w_down, const float* router_bias,
+                                int T, int d, int ffn, int E, int k, moe_dtype dt,
+                                void* out, moe_dtype out_dt,
+                                float* logits_out, float* probs_out, int32_t* counts_out,
+                                hipStream_t stream);
+
 /* ---- Router statistics --------------------------------------------------
  * Source: axonml-nn layers/moe.rs (docs.rs), MoELayer::load_balancing_loss
  * (Switch Transformer form), and MoELayer::expert_utilization for counts.

@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         _p("moe_forward", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp, vp, sz, vp)
         _p("moe_forward_profiled", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp,
            vp, sz, vp, vp)
+        _p("moe_forward_no_alloc", i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, vp, vp, vp,
+           vp)
         _p("moe_router_stats_workspace_size", sz, i, i)
         _p("moe_router_stats", i, vp, vp, i, i, vp, vp, vp, vp, sz, vp)
         _p("moe_forward_ext_workspace_size", sz, i, i, i, i, i, i, vp)
@@ -272,6 +274,36 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, k, router_bias=None, out_dtyp
         assert len(stage_events) == 6
         arr = (ctypes.c_void_p * 6)(*[e.cuda_event for e in stage_events])
         _check(lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
+    return (out, extras) if extras else out
+
+
+NO_ALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NO_ALLOC_SCRATCH_BYTES of include/moe.h
+
+
+def moe_forward_no_alloc(x, w_router, w_gate, w_up, w_down, k, router_bias=None,
+                         out_dtype=torch.float32, out=None, want_logits=False, want_probs=False,
+                         want_counts=False, stream=None):
+    """moe_forward with the library's own fixed scratch instead of a workspace
+    argument (the C call allocates nothing; outputs the caller does not pass
+    are allocated here by torch). Same returns as moe_forward."""
+    _dev(x, w_router, w_gate, w_up, w_down, router_bias, out)
+    T, d, ffn, E = _layer_shapes(x, w_gate, w_up, w_down)
+    assert w_router.shape == (E, d) and w_router.dtype == x.dtype
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=dev)
+    extras = {}
+    if want_logits:
+        extras["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if want_probs:
+        extras["probs"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if want_counts:
+        extras["counts"] = torch.empty(E, dtype=torch.int32, device=dev)
+    _check(lib().moe_forward_no_alloc(
+        _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(router_bias), T, d,
+        ffn, E, k, _dt(x), _ptr(out), _dt(out), _ptr(extras.get("logits")),
+        _ptr(extras.get("probs")), _ptr(extras.get("counts")), _stream(stream)),
+        "moe_forward_no_alloc")
     return (out, extras) if extras else out
 
 

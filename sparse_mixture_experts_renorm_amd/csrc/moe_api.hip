@@ -1,8 +1,10 @@
 // C ABI of the MoE layer: argument checks, workspace carving, kernel launches.
 // Every entry point validates on the host first and enqueues nothing when an
 // argument is rejected. No entry point allocates or frees device memory.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 
@@ -72,6 +74,38 @@ int capacity_rows(float cf, int T, int E, int k) {
   if (cf == 0.f) return T;
   const double c = std::ceil(static_cast<double>(cf) * T * k / E);
   return c >= T ? T : static_cast<int>(c);
+}
+
+}  // namespace
+
+// Scratch of moe_forward_no_alloc: one array per GPU, in the code object's
+// device memory, so that entry point never allocates. In host code the name
+// `scratch` is only a stand-in for the device array; its device address (one
+// per GPU) is looked up once per device and only that address is used.
+static __device__ __align__(256) char scratch[MOE_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with the device current) and kept until the process ends.
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_HIP_ERROR;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_HIP_ERROR;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -323,6 +357,24 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
   }
   return launch_combine_ext(b.y, b.split, b.inv_pos, b.topk_w, T, d, k, w.y_s, w.split_s, S,
                             opt->residual ? x : nullptr, dt, out, out_dt, stream);
+}
+
+moe_status moe_forward_no_alloc(const void* x, const void* w_router, const void* w_gate,
+                                const void* w_up, const void* w_down, const float* router_bias,
+                                int T, int d, int ffn, int E, int k, moe_dtype dt, void* out,
+                                moe_dtype out_dt, float* logits_out, float* probs_out,
+                                int32_t* counts_out, hipStream_t stream) {
+  moe_status st = check_forward(x, w_router, w_gate, w_up, w_down, router_bias, T, d, ffn, E, k,
+                                dt, out, out_dt, logits_out, probs_out, counts_out);
+  if (st != MOE_OK || T == 0) return st;
+  const size_t need = carve_workspace(nullptr, T, d, ffn, E, k, dt).bytes;
+  if (need > static_cast<size_t>(MOE_NO_ALLOC_SCRATCH_BYTES)) return MOE_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(x, w_router, w_gate, w_up, w_down, router_bias, T, d, ffn, E, k, dt, out,
+                      out_dt, logits_out, probs_out, counts_out, ws,
+                      MOE_NO_ALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"

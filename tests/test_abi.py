@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(L):
                           "moe_route_logits", "moe_permute", "moe_expert_ffn", "moe_forward",
                           "moe_forward_profiled", "moe_router_stats_workspace_size",
                           "moe_router_stats", "moe_forward_ext_workspace_size", "moe_forward_ext",
-                          "moe_permute_workspace_size"}
+                          "moe_permute_workspace_size", "moe_forward_no_alloc"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -91,6 +91,28 @@ def test_forward_validation(L):
     # workspace must be 256-byte aligned
     assert L.moe_forward(p, p, p, p, p, None, 16, 64, 64, 4, 2, BF16, p, F32, None, None, None,
                          ctypes.c_void_p(272), 1 << 30, None) == INVALID
+
+
+def test_forward_no_alloc_validation(L):
+    """The fixed-scratch forward checks its arguments as moe_forward does and
+    refuses, on the host, a shape whose workspace exceeds its array."""
+    p = ctypes.c_void_p(256)
+
+    def call(T=16, d=64, ffn=64, E=4, k=2, dt=BF16, out=p):
+        return L.moe_forward_no_alloc(p, p, p, p, p, None, T, d, ffn, E, k, dt, out, F32, None,
+                                      None, None, None)
+
+    assert call(k=0) == INVALID
+    assert call(k=5) == INVALID
+    assert call(d=72) == UNSUPPORTED
+    assert call(out=None) == INVALID
+    assert call(T=0) == OK
+    limit = 64 << 20
+    T = 1
+    while L.moe_workspace_size(T + 1, 4096, 14336, 8, 2, BF16) <= limit:
+        T += 1
+    assert T == 356     # the limit include/moe.h states for the Mixtral widths
+    assert call(T=T + 1, d=4096, ffn=14336, E=8, k=2) == WS_SMALL
 
 
 def test_expert_ffn_and_permute_validation(L):
