@@ -40,6 +40,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Four consecutive values of h, rounded to bf16 (nearest even) into hi[i..];
+// with lo non-null, also the remainder h - hi (exact in fp32) rounded to
+// bf16 into lo[i..], so that hi + lo holds h to about 2^-17 of its value.
+__device__ __forceinline__ void store_h(bf16_t* __restrict__ hi, bf16_t* __restrict__ lo, size_t i,
+                                        const float v[4]) {
+  const uint32_t p0 = pack_bf16x2(v[0], v[1]), p1 = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(hi + i) = make_uint2(p0, p1);
+  if (lo) {
+    const float r0 = v[0] - __uint_as_float(p0 << 16), r1 = v[1] - __uint_as_float(p0 & 0xFFFF0000u);
+    const float r2 = v[2] - __uint_as_float(p1 << 16), r3 = v[3] - __uint_as_float(p1 & 0xFFFF0000u);
+    *reinterpret_cast<uint2*>(lo + i) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+  }
+}
+
 // SiLU(z) = z * sigmoid(z), in fp32.
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -60,6 +74,19 @@ inline moe_status launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
 
+// Whether a bf16 layer carries h into the down pass as two bf16 terms (the
+// rounding of h and the rounding of the remainder): the down pass then does
+// twice the MFMA work, and rounding h to bf16 no longer moves the output.
+// Alone, that rounding moves each output by about 1.6e-3 of its size
+// (relative error of bf16 rounding, RMS), and the largest of many outputs by
+// several times that; with few terms per output (short expert width) or a
+// narrow layer the per-token sizes spread more and the largest error reaches
+// 2e-2 x RMS. Below 1024 in either width the two terms are used.
+constexpr int kTwoTermBelow = 1024;
+inline bool two_term_h(int d, int ffn, moe_dtype dt) {
+  return dt == MOE_BF16 && (d < kTwoTermBelow || ffn < kTwoTermBelow);
+}
+
 // Layout of the caller's workspace (all regions 256-byte aligned).
 struct Workspace {
   int32_t* topk_idx;      // [T*k]
@@ -69,6 +96,7 @@ struct Workspace {
   int32_t* sorted_token;  // [T*k]
   int32_t* inv_pos;       // [T*k]
   void* h;                // [T*k, ffn] in dt
+  void* h_lo;             // [T*k, ffn] bf16: second term of h (two_term_h), else null
   float* y;               // [kMaxDownSplit, T*k, d] fp32 partial sums of the down GEMM
   int32_t* split;         // [1] number of partial sums in y
   int32_t* block_counts;  // [kPermMaxBlocks * E] per-block expert histograms of the permutation
@@ -91,6 +119,7 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   w.sorted_token = reinterpret_cast<int32_t*>(take(tk * 4));
   w.inv_pos = reinterpret_cast<int32_t*>(take(tk * 4));
   w.h = take(tk * static_cast<size_t>(ffn) * es);
+  w.h_lo = two_term_h(d, ffn, dt) ? take(tk * static_cast<size_t>(ffn) * es) : nullptr;
   w.y = reinterpret_cast<float*>(take(kMaxDownSplit * tk * static_cast<size_t>(d) * 4));
   w.split = reinterpret_cast<int32_t*>(take(4));
   w.block_counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(kPermMaxBlocks) * E * 4));
@@ -105,6 +134,7 @@ struct ExtWorkspace {
   int32_t* st_s;          // [n_shared*T] shared experts' rows (identity)
   int32_t* off_s;         // [n_shared+1]
   void* h_s;              // [n_shared*T, shared_ffn] in dt
+  void* h_s_lo;           // second term of h_s (two_term_h for shared_ffn), else null
   float* y_s;             // [kMaxDownSplit, n_shared*T, d] fp32
   int32_t* split_s;       // [1]
   size_t bytes;
@@ -124,6 +154,8 @@ inline ExtWorkspace carve_ext_workspace(void* base, int T, int d, int ffn, int E
     w.st_s = reinterpret_cast<int32_t*>(take(ts * 4));
     w.off_s = reinterpret_cast<int32_t*>(take(static_cast<size_t>(n_shared + 1) * 4));
     w.h_s = take(ts * static_cast<size_t>(shared_ffn) * es);
+    w.h_s_lo = two_term_h(d, shared_ffn, dt) ? take(ts * static_cast<size_t>(shared_ffn) * es)
+                                             : nullptr;
     w.y_s = reinterpret_cast<float*>(take(kMaxDownSplit * ts * static_cast<size_t>(d) * 4));
     w.split_s = reinterpret_cast<int32_t*>(take(4));
   }
@@ -153,17 +185,21 @@ moe_status launch_identity_rows(int T, int S, int32_t* sorted_token, int32_t* of
                                 hipStream_t s);
 moe_status launch_rms_norm(const void* x, const void* g, int T, int d, float eps, moe_dtype dt,
                            void* xn, hipStream_t s);
+// h_lo: null, or (bf16 only) the second bf16 term of h, the rounding of
+// h - h_hi (see store_h); the down pass then multiplies both terms.
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
-                          int k, moe_dtype dt, void* h, hipStream_t s);
-moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down, int T, int d,
-                       int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
+                          int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s);
+moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
+                       int T, int d, int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
                        hipStream_t s);
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
-                                 int d, int ffn, int E, int rows, void* h, hipStream_t s);
-moe_status launch_down_stream(const void* h, const int32_t* offsets, const void* w_down, int d,
-                              int ffn, int E, int rows, float* y, int32_t* split, hipStream_t s);
+                                 int d, int ffn, int E, int rows, void* h, bf16_t* h_lo,
+                                 hipStream_t s);
+moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* offsets,
+                              const void* w_down, int d, int ffn, int E, int rows, float* y,
+                              int32_t* split, hipStream_t s);
 // Few rows per expert: the weight-streaming kernels replace the tiled ones.
 inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
 // Router statistics (router_stats.hip): partial sums over router_stats_blocks(T)

@@ -251,13 +251,24 @@ constexpr int STAGE = TM * TK * 2;  // bytes per operand and stage (32 KB)
 // NW waves per workgroup: 4 (wave tile 128 x 128, one wave per SIMD) or 8
 // (wave tile 128 x 64, two waves per SIMD, so one wave's MFMAs run while the
 // other waits to issue its loads).
-template <bool GATE_UP, int NW, bool KMASK>
+// TWO (down pass only): h is given as two bf16 terms, h = A + Alo (A its
+// rounding to bf16, Alo the rounding of the remainder), and y = A W^T + Alo
+// W^T. A tile then holds 128 rows of y: tile rows 0-127 of the token operand
+// are those rows of A, tile rows 128-255 the same rows of Alo, and the
+// accumulators of token block b and b + 4 (the same output rows) are added
+// in the epilogue. Same loads, MFMAs and barriers per step as one term, so
+// the pass takes about twice as long for the same rows.
+// GATE_UP with Clo non-null writes that second term of h as well.
+template <bool GATE_UP, int NW, bool KMASK, bool TWO = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
-void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
+void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Alo,
+                             const int32_t* __restrict__ sorted_token,
                              const int32_t* __restrict__ offsets, int E,
                              const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
-                             int K, void* __restrict__ Cv, int max_split, int n_cu,
-                             size_t c_split, int32_t* __restrict__ split_out) {
+                             int K, void* __restrict__ Cv, bf16_t* __restrict__ Clo, int max_split,
+                             int n_cu, size_t c_split, int32_t* __restrict__ split_out) {
+  static_assert(!(TWO && GATE_UP), "two terms of h are an operand of the down pass only");
+  constexpr int BM = TWO ? TM / 2 : TM;  // output rows per tile
   // One LDS object per stage and operand. They must be distinct objects: the
   // compiler then sees that the memory-to-LDS loads of the next stage cannot
   // alias the fragment reads of the current one, and does not make those
@@ -274,7 +285,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   Tile tile;
   const int nk = (K + TK - 1) / TK;
   __shared__ int s_map[kMapLdsInts];
-  const bool have = map_tile<TM>(offsets, E, nN, max_split, n_cu, nk, &tile, s_map);
+  const bool have = map_tile<BM>(offsets, E, nN, max_split, n_cu, nk, &tile, s_map);
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;
   // reduction steps [kbeg, kend) of this tile
@@ -297,9 +308,11 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // Tile row r of the weight operand: gate/up rows 0-127 are gate rows
   // n0 .. n0+127, rows 128-255 the same rows of up; down rows are n0 + r.
   const int n0 = GATE_UP ? tile.nt * 128 : tile.nt * TW;
-  const char* a_base = reinterpret_cast<const char*>(A);
+  // with TWO, the waves that load tile rows 128-255 read the second term
+  const char* a_base = reinterpret_cast<const char*>(TWO && wave * IPW * 8 >= BM ? Alo : A);
   const size_t wexp = static_cast<size_t>(tile.e) * N * K * 2;
   auto a_row_off = [&](int r) -> uint32_t {
+    if (TWO) r &= BM - 1;
     // past the valid rows, spread the repeats over all valid rows (one
     // repeated row for a whole load instruction would hit one cache line)
     const int rr = r < tile.rows ? r : r % tile.rows;
@@ -445,7 +458,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // rows (the MFMAs of padding blocks are skipped). Every variant loads the
   // same data and meets the same barriers.
   const int nblk = (tile.rows + 31) / 32;
-  const int nact = nblk - wm >= 7 ? 4 : (nblk - wm >= 5 ? 3 : (nblk - wm >= 3 ? 2 : 1));
+  const int nact = TWO ? 4 : (nblk - wm >= 7 ? 4 : (nblk - wm >= 5 ? 3 : (nblk - wm >= 3 ? 2 : 1)));
   if (nact == 4)
     run(IntC<4>{});
   else if (nact == 3)
@@ -458,8 +471,10 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   // ---- epilogue. acc[nb][mb] element i: token row (wm + 2 mb)*32 + lane%32,
   // weight-tile row (block nb) + 8*(i/4) + 4*(lane/32) + i%4. Gate block nb
   // pairs with up block nb + NBW/2.
+  // With TWO, token block i < 2 of this wave is output rows (wm + 2i)*32 ..
+  // and block i + 2 holds the second term of the same rows.
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < (TWO ? 2 : 4); ++mb) {
     const int m = (wm + 2 * mb) * 32 + (lane & 31);
     if (m >= tile.rows) continue;
     const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
@@ -475,18 +490,21 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               hv[i] = silu_fast(acc[nb][mb][4 * g + i]) * acc[nb + NBW / 2][mb][4 * g + i];
-            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            store_h(static_cast<bf16_t*>(Cv), Clo, crow + n, hv);
           }
         }
       } else {
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
           const int n = tile.nt * TW + wn * NBW * 32 + nb * 32 + nloc;
-          if (n < N)
+          if (n < N) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v[i] = TWO ? acc[nb][mb][4 * g + i] + acc[nb][mb + 2][4 * g + i] : acc[nb][mb][4 * g + i];
             *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
-                make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
-                            acc[nb][mb][4 * g + 3]);
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
     }
@@ -518,8 +536,8 @@ __global__ __launch_bounds__(NW3 * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
 void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
                              const int32_t* __restrict__ offsets, int E,
                              const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
-                             int K, void* __restrict__ Cv, int max_split, int n_cu,
-                             size_t c_split, int32_t* __restrict__ split_out) {
+                             int K, void* __restrict__ Cv, bf16_t* __restrict__ Clo, int max_split,
+                             int n_cu, size_t c_split, int32_t* __restrict__ split_out) {
   __shared__ __attribute__((aligned(1024))) char lds0a[STAGE_A3];
   __shared__ __attribute__((aligned(1024))) char lds0b[STAGE];
   __shared__ __attribute__((aligned(1024))) char lds1a[STAGE_A3];
@@ -715,8 +733,7 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 hv[i] = silu_fast(acc[nb][mb][4 * g + i]) * acc[nb + NB / 2][mb][4 * g + i];
-              *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
-                  make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+              store_h(static_cast<bf16_t*>(Cv), Clo, crow + n, hv);
             }
           }
         } else {
@@ -812,7 +829,7 @@ int cu_count() {
 
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
-                          int k, moe_dtype dt, void* h, hipStream_t s) {
+                          int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s) {
   const int rows = T * k;
   if (dt == MOE_F32) {
     expert_gemm_f32_kernel<true><<<dim3(rows, (ffn + 255) / 256), 256, 0, s>>>(
@@ -820,25 +837,27 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
         static_cast<const float*>(w_up), ffn, d, static_cast<float*>(h), nullptr);
     return launch_status();
   }
+  bf16_t* hl = static_cast<bf16_t*>(h_lo);
   if (use_stream_path(rows, E))
-    return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows, h, s);
+    return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows, h, hl, s);
   if (use_tall_tiles(rows, E)) {
     auto kern = d % TK ? expert_gemm_tall_kernel<true, true> : expert_gemm_tall_kernel<true, false>;
     const int ncu = cu_count();
     kern<<<tall_grid(rows, E, (ffn + 127) / 128, 1, ncu), NW3 * 64, 0, s>>>(
         static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
-        static_cast<const bf16_t*>(w_up), ffn, d, h, 1, ncu, 0, nullptr);
+        static_cast<const bf16_t*>(w_up), ffn, d, h, hl, 1, ncu, 0, nullptr);
     return launch_status();
   }
   auto kern = d % TK ? expert_gemm_bf16_kernel<true, kWaves, true> : expert_gemm_bf16_kernel<true, kWaves, false>;
   kern<<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), kWaves * 64, 0, s>>>(
-      static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
-      static_cast<const bf16_t*>(w_up), ffn, d, h, 1, cu_count(), 0, nullptr);
+      static_cast<const bf16_t*>(x), nullptr, sorted_token, offsets, E,
+      static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), ffn, d, h, hl, 1,
+      cu_count(), 0, nullptr);
   return launch_status();
 }
 
-moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down, int T, int d,
-                       int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
+moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
+                       int T, int d, int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
                        hipStream_t s) {
   const int rows = T * k;
   if (dt == MOE_F32) {
@@ -847,19 +866,33 @@ moe_status launch_down(const void* h, const int32_t* offsets, const void* w_down
         nullptr, d, ffn, y, split);
     return launch_status();
   }
-  if (use_stream_path(rows, E)) return launch_down_stream(h, offsets, w_down, d, ffn, E, rows, y, split, s);
+  const bf16_t* hl = static_cast<const bf16_t*>(h_lo);
+  if (use_stream_path(rows, E))
+    return launch_down_stream(h, hl, offsets, w_down, d, ffn, E, rows, y, split, s);
+  const size_t c_split = static_cast<size_t>(rows) * d;
+  if (hl) {
+    // two terms of h: 128 output rows per 256 x 256 tile
+    auto kern = ffn % TK ? expert_gemm_bf16_kernel<false, kWaves, true, true>
+                         : expert_gemm_bf16_kernel<false, kWaves, false, true>;
+    kern<<<tile_grid(rows, E, TM / 2, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64, 0, s>>>(
+        static_cast<const bf16_t*>(h), hl, nullptr, offsets, E,
+        static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, nullptr, kMaxDownSplit, cu_count(),
+        c_split, split);
+    return launch_status();
+  }
   if (use_tall_tiles(rows, E)) {
     auto kern = ffn % TK ? expert_gemm_tall_kernel<false, true> : expert_gemm_tall_kernel<false, false>;
     const int ncu = cu_count();
     kern<<<tall_grid(rows, E, (d + TW - 1) / TW, kMaxDownSplit, ncu), NW3 * 64, 0, s>>>(
         static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
-        nullptr, d, ffn, y, kMaxDownSplit, ncu, static_cast<size_t>(rows) * d, split);
+        nullptr, d, ffn, y, nullptr, kMaxDownSplit, ncu, c_split, split);
     return launch_status();
   }
   auto kern = ffn % TK ? expert_gemm_bf16_kernel<false, kWaves, true> : expert_gemm_bf16_kernel<false, kWaves, false>;
   kern<<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64, 0, s>>>(
-      static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
-      nullptr, d, ffn, y, kMaxDownSplit, cu_count(), static_cast<size_t>(rows) * d, split);
+      static_cast<const bf16_t*>(h), nullptr, nullptr, offsets, E,
+      static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, nullptr, kMaxDownSplit, cu_count(),
+      c_split, split);
   return launch_status();
 }
 

@@ -49,18 +49,24 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
 }
 
 // One pass over reduction range [kbeg, kend) (kbeg a multiple of 64) for
-// token rows mb .. mb + 16*NB of expert rows starting at row0.
-template <bool GATE_UP, int RB, int NB>
+// token rows mb .. mb + 16*NB of expert rows starting at row0. TWO (down
+// only): h comes as two bf16 terms, A and Alo, and both are multiplied into
+// the same accumulators. GATE_UP with Clo non-null also writes the second
+// term of h.
+template <bool GATE_UP, int RB, int NB, bool TWO>
 __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
+                                            const bf16_t* __restrict__ Alo,
                                             const int32_t* __restrict__ sorted_token,
                                             const bf16_t* const (&wg)[RB],
                                             const bf16_t* const (&wu)[RB], int row0, int rows,
                                             int mb, int n0, int N, int K, int kbeg, int kend,
-                                            void* __restrict__ Cv, int lane) {
+                                            void* __restrict__ Cv, bf16_t* __restrict__ Clo,
+                                            int lane) {
   const int r16 = lane & 15, q = lane >> 4;
   const int lr = lane >> 2, lp = lane & 3;  // load layout: row lane/4, piece lane%4
   const int xa = 4 * (4 * r16 + q);
   const bf16_t* ap[NB];
+  const bf16_t* apl[NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     int m = mb + t * 16 + lr;
@@ -68,6 +74,7 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
     const size_t arow = GATE_UP ? static_cast<size_t>(sorted_token[row0 + m])
                                 : static_cast<size_t>(row0 + m);
     ap[t] = A + arow * K + lp * 8;
+    apl[t] = TWO ? Alo + arow * K + lp * 8 : nullptr;
   }
   f32x4 accg[RB][NB], accu[RB][NB];
 #pragma unroll
@@ -78,7 +85,7 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
       for (int i = 0; i < 4; ++i) accg[r][t][i] = accu[r][t][i] = 0.f;
 
   // chunk = two 32-wide steps; slot s holds one chunk
-  uint4 bw[DEPTH][RB][2], bu[DEPTH][RB][2], ba[DEPTH][NB][2];
+  uint4 bw[DEPTH][RB][2], bu[DEPTH][RB][2], ba[DEPTH][NB][2], bl[DEPTH][TWO ? NB : 1][2];
   auto load = [&](int k0, int s) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -88,20 +95,29 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
         if (GATE_UP) bu[s][r][j] = ld16(wu[r] + k0 + 32 * j);
       }
 #pragma unroll
-      for (int t = 0; t < NB; ++t) ba[s][t][j] = ld16(ap[t] + k0 + 32 * j);
+      for (int t = 0; t < NB; ++t) {
+        ba[s][t][j] = ld16(ap[t] + k0 + 32 * j);
+        if (TWO) bl[s][t][j] = ld16(apl[t] + k0 + 32 * j);
+      }
     }
   };
   auto mma = [&](int s) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      uint4 a[NB];
+      uint4 a[NB], al[TWO ? NB : 1];
 #pragma unroll
-      for (int t = 0; t < NB; ++t) a[t] = xpose(ba[s][t][j], xa);
+      for (int t = 0; t < NB; ++t) {
+        a[t] = xpose(ba[s][t][j], xa);
+        if (TWO) al[t] = xpose(bl[s][t][j], xa);
+      }
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const uint4 g = xpose(bw[s][r][j], xa);
 #pragma unroll
-        for (int t = 0; t < NB; ++t) accg[r][t] = mfma16(g, a[t], accg[r][t]);
+        for (int t = 0; t < NB; ++t) {
+          accg[r][t] = mfma16(g, a[t], accg[r][t]);
+          if (TWO) accg[r][t] = mfma16(g, al[t], accg[r][t]);
+        }
         if (GATE_UP) {
           const uint4 u = xpose(bu[s][r][j], xa);
 #pragma unroll
@@ -130,14 +146,20 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
   for (int k0 = kbeg + 64 * nchunks; k0 < kend; k0 += 32) {
     const bool in = k0 + lp * 8 < kend;
     const uint4 z = make_uint4(0, 0, 0, 0);
-    uint4 a[NB];
+    uint4 a[NB], al[TWO ? NB : 1];
 #pragma unroll
-    for (int t = 0; t < NB; ++t) a[t] = xpose(in ? ld16(ap[t] + k0) : z, xa);
+    for (int t = 0; t < NB; ++t) {
+      a[t] = xpose(in ? ld16(ap[t] + k0) : z, xa);
+      if (TWO) al[t] = xpose(in ? ld16(apl[t] + k0) : z, xa);
+    }
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const uint4 g = xpose(in ? ld16(wg[r] + k0) : z, xa);
 #pragma unroll
-      for (int t = 0; t < NB; ++t) accg[r][t] = mfma16(g, a[t], accg[r][t]);
+      for (int t = 0; t < NB; ++t) {
+        accg[r][t] = mfma16(g, a[t], accg[r][t]);
+        if (TWO) accg[r][t] = mfma16(g, al[t], accg[r][t]);
+      }
       if (GATE_UP) {
         const uint4 u = xpose(in ? ld16(wu[r] + k0) : z, xa);
 #pragma unroll
@@ -160,8 +182,7 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
         float hv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hv[i] = silu_fast(accg[r][t][i]) * accu[r][t][i];
-        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cv) + crow + n) =
-            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+        store_h(static_cast<bf16_t*>(Cv), Clo, crow + n, hv);
       } else {
         *reinterpret_cast<float4*>(static_cast<float*>(Cv) + crow + n) =
             make_float4(accg[r][t][0], accg[r][t][1], accg[r][t][2], accg[r][t][3]);
@@ -171,14 +192,18 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
 }
 
 // Grid: (ceil(N / (16 * RB * SW)), E, S). GATE_UP: A = x gathered by
-// sorted_token, weight rows from w_gate and w_up, C = h (bf16). !GATE_UP:
-// A = h rows, weights w_down, C = y (fp32), part z at C + z * c_split.
-template <bool GATE_UP, int RB, int NB>
+// sorted_token, weight rows from w_gate and w_up, C = h (bf16; with Clo
+// non-null its second term goes there). !GATE_UP: A = h rows (TWO: plus
+// their second terms Alo), weights w_down, C = y (fp32), part z at
+// C + z * c_split.
+template <bool GATE_UP, int RB, int NB, bool TWO = false>
 __global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
-    const int32_t* __restrict__ offsets, const bf16_t* __restrict__ B0,
-    const bf16_t* __restrict__ B1, int N, int K, void* __restrict__ Cv, size_t c_split,
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ Alo,
+    const int32_t* __restrict__ sorted_token, const int32_t* __restrict__ offsets,
+    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N, int K,
+    void* __restrict__ Cv, bf16_t* __restrict__ Clo, size_t c_split,
     int32_t* __restrict__ split_out) {
+  static_assert(!(TWO && GATE_UP), "two terms of h are an operand of the down pass only");
   const int S = gridDim.z, z = blockIdx.z;
   if (!GATE_UP && split_out && blockIdx.x == 0 && blockIdx.y == 0 && z == 0 && threadIdx.x == 0)
     *split_out = S;
@@ -204,8 +229,8 @@ __global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
   }
   void* C = GATE_UP ? Cv : static_cast<void*>(static_cast<float*>(Cv) + z * c_split);
   for (int mb = 0; mb < rows; mb += 16 * NB)
-    stream_pass<GATE_UP, RB, NB>(A, sorted_token, wg, wu, row0, rows, mb, n0, N, K, kbeg, kend, C,
-                             lane);
+    stream_pass<GATE_UP, RB, NB, TWO>(A, Alo, sorted_token, wg, wu, row0, rows, mb, n0, N, K,
+                                      kbeg, kend, C, Clo, lane);
 }
 
 // 16-row token blocks per pass: enough for the average expert of the batch.
@@ -219,21 +244,24 @@ constexpr int kRbGateUp = 1, kRbDown = 2;
 
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
-                                 int d, int ffn, int E, int rows, void* h, hipStream_t s) {
+                                 int d, int ffn, int E, int rows, void* h, bf16_t* h_lo,
+                                 hipStream_t s) {
   constexpr int RB = kRbGateUp;
   dim3 grid((ffn + 16 * RB * SW - 1) / (16 * RB * SW), E, 1);
   auto run = [&](auto kern) {
-    kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(x), sorted_token, offsets,
+    kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(x), nullptr, sorted_token, offsets,
                                   static_cast<const bf16_t*>(w_gate),
-                                  static_cast<const bf16_t*>(w_up), ffn, d, h, size_t(0), nullptr);
+                                  static_cast<const bf16_t*>(w_up), ffn, d, h, h_lo, size_t(0),
+                                  nullptr);
   };
   if (token_blocks(rows, E) == 1) run(expert_stream_kernel<true, RB, 1>);
   else run(expert_stream_kernel<true, RB, 2>);
   return launch_status();
 }
 
-moe_status launch_down_stream(const void* h, const int32_t* offsets, const void* w_down, int d,
-                              int ffn, int E, int rows, float* y, int32_t* split, hipStream_t s) {
+moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* offsets,
+                              const void* w_down, int d, int ffn, int E, int rows, float* y,
+                              int32_t* split, hipStream_t s) {
   constexpr int RB = kRbDown;
   // cut the reduction (into whole 64-wide chunks, at least 16 per part)
   // until the grid holds about two waves per SIMD
@@ -243,12 +271,18 @@ moe_status launch_down_stream(const void* h, const int32_t* offsets, const void*
   dim3 grid(nx, E, S);
   const size_t c_split = static_cast<size_t>(rows) * d;
   auto run = [&](auto kern) {
-    kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(h), nullptr, offsets,
-                                  static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, c_split,
-                                  split);
+    kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(h), h_lo, nullptr, offsets,
+                                  static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, nullptr,
+                                  c_split, split);
   };
-  if (token_blocks(rows, E) == 1) run(expert_stream_kernel<false, RB, 1>);
-  else run(expert_stream_kernel<false, RB, 2>);
+  const bool one = token_blocks(rows, E) == 1;
+  if (h_lo) {
+    if (one) run(expert_stream_kernel<false, RB, 1, true>);
+    else run(expert_stream_kernel<false, RB, 2, true>);
+  } else {
+    if (one) run(expert_stream_kernel<false, RB, 1>);
+    else run(expert_stream_kernel<false, RB, 2>);
+  }
   return launch_status();
 }
 

@@ -207,10 +207,11 @@ static moe_status run_experts(const void* x, const int32_t* topk_idx, const floa
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[2], stream);
   st = launch_gate_up(x, ws.sorted_token, ws.offsets, w_gate, w_up, T, d, ffn, E, k, dt, ws.h,
-                      stream);
+                      ws.h_lo, stream);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], stream);
-  st = launch_down(ws.h, ws.offsets, w_down, T, d, ffn, E, k, dt, ws.y, ws.split, stream);
+  st = launch_down(ws.h, ws.h_lo, ws.offsets, w_down, T, d, ffn, E, k, dt, ws.y, ws.split,
+                   stream);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[4], stream);
   st = launch_combine(ws.y, ws.split, ws.inv_pos, topk_w, T, d, k, out, out_dt, stream);
@@ -340,19 +341,19 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
                       b.sorted_token, b.inv_pos, b.block_counts, stream);
   if (st != MOE_OK) return st;
   st = launch_gate_up(xl, b.sorted_token, b.offsets, w_gate, w_up, T, d, ffn, E, k, dt, b.h,
-                      stream);
+                      b.h_lo, stream);
   if (st != MOE_OK) return st;
-  st = launch_down(b.h, b.offsets, w_down, T, d, ffn, E, k, dt, b.y, b.split, stream);
+  st = launch_down(b.h, b.h_lo, b.offsets, w_down, T, d, ffn, E, k, dt, b.y, b.split, stream);
   if (st != MOE_OK) return st;
   if (S > 0) {
     // shared experts: S more experts that every token reaches, T rows each
     st = launch_identity_rows(T, S, w.st_s, w.off_s, stream);
     if (st != MOE_OK) return st;
     st = launch_gate_up(xl, w.st_s, w.off_s, opt->shared_gate, opt->shared_up, T, d,
-                        opt->shared_ffn, S, S, dt, w.h_s, stream);
+                        opt->shared_ffn, S, S, dt, w.h_s, w.h_s_lo, stream);
     if (st != MOE_OK) return st;
-    st = launch_down(w.h_s, w.off_s, opt->shared_down, T, d, opt->shared_ffn, S, S, dt, w.y_s,
-                     w.split_s, stream);
+    st = launch_down(w.h_s, w.h_s_lo, w.off_s, opt->shared_down, T, d, opt->shared_ffn, S, S, dt,
+                     w.y_s, w.split_s, stream);
     if (st != MOE_OK) return st;
   }
   return launch_combine_ext(b.y, b.split, b.inv_pos, b.topk_w, T, d, k, w.y_s, w.split_s, S,

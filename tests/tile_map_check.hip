@@ -117,7 +117,9 @@ int main() {
     const int n_cu = cus[it % 5];
     if (check<256, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
     if (check<384, true>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
-    cases += 2;
+    // the down pass with h in two bf16 terms: 128 output rows per tile
+    if (check<128, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
+    cases += 3;
   }
   printf("ok: %d cases, %lld tiles\n", cases, tiles);
   return 0;
