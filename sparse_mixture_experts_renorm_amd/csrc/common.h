@@ -193,13 +193,16 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
 moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
                        int T, int d, int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
                        hipStream_t s);
+// Weight-streaming kernels; experts with more than max_rows rows are skipped
+// (left to a tiled launch). The down pass cuts its reduction into at most
+// max_split parts.
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
                                  int d, int ffn, int E, int rows, void* h, bf16_t* h_lo,
-                                 hipStream_t s);
+                                 int max_rows, hipStream_t s);
 moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* offsets,
                               const void* w_down, int d, int ffn, int E, int rows, float* y,
-                              int32_t* split, hipStream_t s);
+                              int32_t* split, int max_rows, int max_split, hipStream_t s);
 // Few rows per expert: the weight-streaming kernels replace the tiled ones.
 inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
 // Router statistics (router_stats.hip): partial sums over router_stats_blocks(T)

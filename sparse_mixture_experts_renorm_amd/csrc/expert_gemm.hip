@@ -69,14 +69,19 @@ struct Tile {
 };
 
 // Row tiles of BM rows per expert, as a prefix: pref[e] = sum over e' < e of
-// ceil(M_e' / BM), for e = 0 .. E (M_e = offsets[e+1] - offsets[e]).
-// Serial form, for the host; the kernels build the same array with one wave
-// (map_tile).
+// ceil(M_e' / BM), for e = 0 .. E (M_e = offsets[e+1] - offsets[e]); experts
+// with at most min_rows rows get no tiles (the weight-streaming kernel takes
+// them). Serial form, for the host; the kernels build the same array with
+// one wave (map_tile).
+__host__ __device__ inline int expert_row_tiles(int m, int BM, int min_rows) {
+  return m > min_rows ? (m + BM - 1) / BM : 0;
+}
 template <int BM>
 __host__ __device__ inline void row_tile_prefix(const int32_t* __restrict__ offsets, int E,
-                                                int* pref) {
+                                                int* pref, int min_rows = 0) {
   pref[0] = 0;
-  for (int e = 0; e < E; ++e) pref[e + 1] = pref[e] + (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+  for (int e = 0; e < E; ++e)
+    pref[e + 1] = pref[e] + expert_row_tiles(offsets[e + 1] - offsets[e], BM, min_rows);
 }
 
 // Tile of workgroup `block` among tiles of BM rows, given the experts' row
@@ -172,7 +177,7 @@ static_assert(kMaxExperts <= 4 * kWave, "map_tile sums four experts per lane");
 // thread 0 runs assign_tile on it. s_map: kMapLdsInts ints of LDS.
 template <int BM, bool TAIL = false>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
-                         int n_cu, int nk, Tile* out, int* s_map) {
+                         int n_cu, int nk, int min_rows, Tile* out, int* s_map) {
   int* pref = s_map + 8;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
@@ -180,7 +185,7 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
-      c[q] = e < E ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+      c[q] = e < E ? expert_row_tiles(offsets[e + 1] - offsets[e], BM, min_rows) : 0;
       sum += c[q];
     }
     int incl = sum;
@@ -266,7 +271,8 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restr
                              const int32_t* __restrict__ offsets, int E,
                              const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
                              int K, void* __restrict__ Cv, bf16_t* __restrict__ Clo, int max_split,
-                             int n_cu, size_t c_split, int32_t* __restrict__ split_out) {
+                             int n_cu, size_t c_split, int32_t* __restrict__ split_out,
+                             int min_rows) {
   static_assert(!(TWO && GATE_UP), "two terms of h are an operand of the down pass only");
   constexpr int BM = TWO ? TM / 2 : TM;  // output rows per tile
   // One LDS object per stage and operand. They must be distinct objects: the
@@ -285,7 +291,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restr
   Tile tile;
   const int nk = (K + TK - 1) / TK;
   __shared__ int s_map[kMapLdsInts];
-  const bool have = map_tile<BM>(offsets, E, nN, max_split, n_cu, nk, &tile, s_map);
+  const bool have = map_tile<BM>(offsets, E, nN, max_split, n_cu, nk, min_rows, &tile, s_map);
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;
   // reduction steps [kbeg, kend) of this tile
@@ -537,7 +543,8 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
                              const int32_t* __restrict__ offsets, int E,
                              const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
                              int K, void* __restrict__ Cv, bf16_t* __restrict__ Clo, int max_split,
-                             int n_cu, size_t c_split, int32_t* __restrict__ split_out) {
+                             int n_cu, size_t c_split, int32_t* __restrict__ split_out,
+                             int min_rows) {
   __shared__ __attribute__((aligned(1024))) char lds0a[STAGE_A3];
   __shared__ __attribute__((aligned(1024))) char lds0b[STAGE];
   __shared__ __attribute__((aligned(1024))) char lds1a[STAGE_A3];
@@ -548,7 +555,7 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
   const int nk = (K + TK - 1) / TK;
-  const bool have = map_tile<TM3, true>(offsets, E, nN, max_split, n_cu, nk, &tile,
+  const bool have = map_tile<TM3, true>(offsets, E, nN, max_split, n_cu, nk, min_rows, &tile,
                                         reinterpret_cast<int*>(lds1a));
   __syncthreads();
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
@@ -825,6 +832,26 @@ int cu_count() {
   return n;
 }
 
+// Weight streaming for few rows per expert: an expert may still hold up to
+// min(T, cap) rows, and the streaming kernel reads its weights once per 32
+// of them; above kStreamMaxRows rows it is left to a 256 x 256 tile launch
+// after the streaming one (only when T allows such an expert at all).
+constexpr int kStreamMaxRows = 64;
+inline bool stream_needs_tiles(int T) { return T > kStreamMaxRows; }
+
+template <bool GATE_UP, bool TWO>
+void launch_256(const bf16_t* A, const bf16_t* Alo, const int32_t* sorted_token,
+                const int32_t* offsets, int E, const bf16_t* B0, const bf16_t* B1, int N, int K,
+                void* C, bf16_t* Clo, int rows, int max_split, size_t c_split, int32_t* split,
+                int min_rows, hipStream_t s) {
+  auto kern = K % TK ? expert_gemm_bf16_kernel<GATE_UP, kWaves, true, TWO>
+                     : expert_gemm_bf16_kernel<GATE_UP, kWaves, false, TWO>;
+  const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
+  kern<<<tile_grid(rows, E, TWO ? TM / 2 : TM, nN, max_split), kWaves * 64, 0, s>>>(
+      A, Alo, sorted_token, offsets, E, B0, B1, N, K, C, Clo, max_split, cu_count(), c_split,
+      split, min_rows);
+}
+
 }  // namespace
 
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
@@ -838,21 +865,27 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
     return launch_status();
   }
   bf16_t* hl = static_cast<bf16_t*>(h_lo);
-  if (use_stream_path(rows, E))
-    return launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows, h, hl, s);
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const bf16_t* wg = static_cast<const bf16_t*>(w_gate);
+  const bf16_t* wu = static_cast<const bf16_t*>(w_up);
+  if (use_stream_path(rows, E)) {
+    const bool tiles = stream_needs_tiles(T);
+    moe_status st = launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows,
+                                          h, hl, tiles ? kStreamMaxRows : T, s);
+    if (st != MOE_OK || !tiles) return st;
+    launch_256<true, false>(xb, nullptr, sorted_token, offsets, E, wg, wu, ffn, d, h, hl, rows, 1,
+                            0, nullptr, kStreamMaxRows, s);
+    return launch_status();
+  }
   if (use_tall_tiles(rows, E)) {
     auto kern = d % TK ? expert_gemm_tall_kernel<true, true> : expert_gemm_tall_kernel<true, false>;
     const int ncu = cu_count();
     kern<<<tall_grid(rows, E, (ffn + 127) / 128, 1, ncu), NW3 * 64, 0, s>>>(
-        static_cast<const bf16_t*>(x), sorted_token, offsets, E, static_cast<const bf16_t*>(w_gate),
-        static_cast<const bf16_t*>(w_up), ffn, d, h, hl, 1, ncu, 0, nullptr);
+        xb, sorted_token, offsets, E, wg, wu, ffn, d, h, hl, 1, ncu, 0, nullptr, 0);
     return launch_status();
   }
-  auto kern = d % TK ? expert_gemm_bf16_kernel<true, kWaves, true> : expert_gemm_bf16_kernel<true, kWaves, false>;
-  kern<<<tile_grid(rows, E, TM, (ffn + 127) / 128, 1), kWaves * 64, 0, s>>>(
-      static_cast<const bf16_t*>(x), nullptr, sorted_token, offsets, E,
-      static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), ffn, d, h, hl, 1,
-      cu_count(), 0, nullptr);
+  launch_256<true, false>(xb, nullptr, sorted_token, offsets, E, wg, wu, ffn, d, h, hl, rows, 1, 0,
+                          nullptr, 0, s);
   return launch_status();
 }
 
@@ -866,33 +899,41 @@ moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, 
         nullptr, d, ffn, y, split);
     return launch_status();
   }
+  const bf16_t* hb = static_cast<const bf16_t*>(h);
   const bf16_t* hl = static_cast<const bf16_t*>(h_lo);
-  if (use_stream_path(rows, E))
-    return launch_down_stream(h, hl, offsets, w_down, d, ffn, E, rows, y, split, s);
+  const bf16_t* wd = static_cast<const bf16_t*>(w_down);
   const size_t c_split = static_cast<size_t>(rows) * d;
+  if (use_stream_path(rows, E)) {
+    // with a tile launch as well, both write one partial sum (the combine
+    // reads one count of parts for every row)
+    const bool tiles = stream_needs_tiles(T);
+    moe_status st = launch_down_stream(h, hl, offsets, w_down, d, ffn, E, rows, y, split,
+                                       tiles ? kStreamMaxRows : T, tiles ? 1 : kMaxDownSplit, s);
+    if (st != MOE_OK || !tiles) return st;
+    if (hl)
+      launch_256<false, true>(hb, hl, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, rows,
+                              1, c_split, split, kStreamMaxRows, s);
+    else
+      launch_256<false, false>(hb, nullptr, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr,
+                               rows, 1, c_split, split, kStreamMaxRows, s);
+    return launch_status();
+  }
   if (hl) {
     // two terms of h: 128 output rows per 256 x 256 tile
-    auto kern = ffn % TK ? expert_gemm_bf16_kernel<false, kWaves, true, true>
-                         : expert_gemm_bf16_kernel<false, kWaves, false, true>;
-    kern<<<tile_grid(rows, E, TM / 2, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64, 0, s>>>(
-        static_cast<const bf16_t*>(h), hl, nullptr, offsets, E,
-        static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, nullptr, kMaxDownSplit, cu_count(),
-        c_split, split);
+    launch_256<false, true>(hb, hl, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, rows,
+                            kMaxDownSplit, c_split, split, 0, s);
     return launch_status();
   }
   if (use_tall_tiles(rows, E)) {
     auto kern = ffn % TK ? expert_gemm_tall_kernel<false, true> : expert_gemm_tall_kernel<false, false>;
     const int ncu = cu_count();
     kern<<<tall_grid(rows, E, (d + TW - 1) / TW, kMaxDownSplit, ncu), NW3 * 64, 0, s>>>(
-        static_cast<const bf16_t*>(h), nullptr, offsets, E, static_cast<const bf16_t*>(w_down),
-        nullptr, d, ffn, y, nullptr, kMaxDownSplit, ncu, c_split, split);
+        hb, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, kMaxDownSplit, ncu, c_split,
+        split, 0);
     return launch_status();
   }
-  auto kern = ffn % TK ? expert_gemm_bf16_kernel<false, kWaves, true> : expert_gemm_bf16_kernel<false, kWaves, false>;
-  kern<<<tile_grid(rows, E, TM, (d + TW - 1) / TW, kMaxDownSplit), kWaves * 64, 0, s>>>(
-      static_cast<const bf16_t*>(h), nullptr, nullptr, offsets, E,
-      static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, nullptr, kMaxDownSplit, cu_count(),
-      c_split, split);
+  launch_256<false, false>(hb, nullptr, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, rows,
+                           kMaxDownSplit, c_split, split, 0, s);
   return launch_status();
 }
 

@@ -20,7 +20,9 @@
 //     chunks ahead;
 //   - the down GEMM may cut the reduction into S parts (blockIdx.z), each
 //     writing its own fp32 partial; the combine sums the parts in order;
-//   - experts without rows exit at once, so their weights are never read.
+//   - experts without rows exit at once, so their weights are never read;
+//     so do experts with more than max_rows rows, which a tiled launch takes
+//     (their weights would otherwise be read once per 16*NB rows).
 // Token rows past an expert's count repeat a valid row; their results are
 // never stored.
 #include "common.h"
@@ -202,14 +204,14 @@ __global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
     const int32_t* __restrict__ sorted_token, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N, int K,
     void* __restrict__ Cv, bf16_t* __restrict__ Clo, size_t c_split,
-    int32_t* __restrict__ split_out) {
+    int32_t* __restrict__ split_out, int max_rows) {
   static_assert(!(TWO && GATE_UP), "two terms of h are an operand of the down pass only");
   const int S = gridDim.z, z = blockIdx.z;
   if (!GATE_UP && split_out && blockIdx.x == 0 && blockIdx.y == 0 && z == 0 && threadIdx.x == 0)
     *split_out = S;
   const int e = blockIdx.y;
   const int row0 = offsets[e], rows = offsets[e + 1] - row0;
-  if (rows == 0) return;
+  if (rows == 0 || rows > max_rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * SW + wave) * 16 * RB;
   if (n0 >= N) return;
@@ -245,14 +247,14 @@ constexpr int kRbGateUp = 1, kRbDown = 2;
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
                                  int d, int ffn, int E, int rows, void* h, bf16_t* h_lo,
-                                 hipStream_t s) {
+                                 int max_rows, hipStream_t s) {
   constexpr int RB = kRbGateUp;
   dim3 grid((ffn + 16 * RB * SW - 1) / (16 * RB * SW), E, 1);
   auto run = [&](auto kern) {
     kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(x), nullptr, sorted_token, offsets,
                                   static_cast<const bf16_t*>(w_gate),
                                   static_cast<const bf16_t*>(w_up), ffn, d, h, h_lo, size_t(0),
-                                  nullptr);
+                                  nullptr, max_rows);
   };
   if (token_blocks(rows, E) == 1) run(expert_stream_kernel<true, RB, 1>);
   else run(expert_stream_kernel<true, RB, 2>);
@@ -261,19 +263,19 @@ moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
 
 moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* offsets,
                               const void* w_down, int d, int ffn, int E, int rows, float* y,
-                              int32_t* split, hipStream_t s) {
+                              int32_t* split, int max_rows, int max_split, hipStream_t s) {
   constexpr int RB = kRbDown;
   // cut the reduction (into whole 64-wide chunks, at least 16 per part)
   // until the grid holds about two waves per SIMD
   const int nx = (d + 16 * RB * SW - 1) / (16 * RB * SW);
   int S = 1;
-  while (2 * S <= kMaxDownSplit && nx * E * S * SW < 2048 && ffn / 64 >= 2 * S * 16) S *= 2;
+  while (2 * S <= max_split && nx * E * S * SW < 2048 && ffn / 64 >= 2 * S * 16) S *= 2;
   dim3 grid(nx, E, S);
   const size_t c_split = static_cast<size_t>(rows) * d;
   auto run = [&](auto kern) {
     kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(h), h_lo, nullptr, offsets,
                                   static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, nullptr,
-                                  c_split, split);
+                                  c_split, split, max_rows);
   };
   const bool one = token_blocks(rows, E) == 1;
   if (h_lo) {

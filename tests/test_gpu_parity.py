@@ -131,6 +131,12 @@ EXPERT_SHAPES = [
     (40, 272, 336, 4, 2, "bf16", "random"),      # ragged K tails on both passes
     (60, 128, 192, 4, 2, "bf16", "all_same"),    # 60 rows on experts 0 and 1 (two row blocks)
     (16, 64, 96, 8, 1, "bf16", "one_heavy"),     # k = 1, every token on expert 7
+    # streaming path with an expert above 64 rows: that expert goes to a tile
+    # launch after the streaming one (instead of reading its weights once per
+    # 32 rows)
+    (256, 64, 96, 8, 1, "bf16", "one_heavy"),    # all 256 rows on expert 7
+    (128, 256, 320, 8, 2, "bf16", "one_heavy"),  # expert 7 tiled (two-term h), the rest streamed
+    (100, 1024, 1024, 4, 1, "bf16", "all_same"),  # one-term h, all 100 rows on expert 0
     (32, 4096, 14336, 8, 2, "bf16", "random"),   # decode shape
     # at least 768 rows per expert on average: the tall-tile kernels
     (3200, 256, 320, 4, 1, "bf16", "random"),

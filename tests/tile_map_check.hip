@@ -18,7 +18,7 @@ using namespace moe;
 
 template <int BM, bool TAIL>
 static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN, int max_split,
-                 int n_cu, int nk, long long* tiles_seen) {
+                 int n_cu, int nk, long long* tiles_seen, int min_rows = 0) {
   const unsigned grid = TAIL ? tall_grid(rows_bound, E, nN, max_split, n_cu)
                              : tile_grid(rows_bound, E, BM, nN, max_split);
   // key (e, row tile, column tile, part) -> counts {whole, half 0, half 1}
@@ -27,7 +27,7 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
   std::map<std::tuple<int, int, int, int>, int> rows_of;
   int S = -1;
   std::vector<int> pref(E + 1);
-  row_tile_prefix<BM>(off.data(), E, pref.data());
+  row_tile_prefix<BM>(off.data(), E, pref.data(), min_rows);
   for (unsigned b = 0; b < grid; ++b) {
     int res[7];
     assign_tile<BM, TAIL>(off.data(), pref.data(), E, nN, max_split, n_cu, nk, static_cast<int>(b), res);
@@ -35,6 +35,8 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
     if (res[5] != S) return printf("split count differs between workgroups\n"), 1;
     if (res[0] < 0) continue;
     const int e = res[0];
+    if (e >= 0 && e < E && off[e + 1] - off[e] <= min_rows)
+      return printf("expert %d with %d rows (at most %d) got a tile\n", e, off[e + 1] - off[e], min_rows), 1;
     if (e >= E || res[1] < off[e] || res[1] % 32 != off[e] % 32 || res[2] <= 0 || res[2] > BM ||
         res[1] + res[2] > off[e + 1] || res[3] < 0 || res[3] >= nN || res[4] < 0 ||
         res[4] >= S || res[6] < -1 || res[6] > 1 || (!TAIL && res[6] != -1))
@@ -70,12 +72,12 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
       }
       if (next != off[e + 1]) return printf("row tiles of expert %d do not reach its end\n", e), 1;
       if (hi - lo > 1) return printf("row tiles of expert %d are uneven: %d..%d blocks\n", e, lo, hi), 1;
-      if (static_cast<int>(v.size()) != (off[e + 1] - off[e] + BM - 1) / BM)
+      if (static_cast<int>(v.size()) != expert_row_tiles(off[e + 1] - off[e], BM, min_rows))
         return printf("expert %d has %zu row tiles\n", e, v.size()), 1;
     }
   }
   long long expected = 0;
-  for (int e = 0; e < E; ++e) expected += static_cast<long long>((off[e + 1] - off[e] + BM - 1) / BM);
+  for (int e = 0; e < E; ++e) expected += expert_row_tiles(off[e + 1] - off[e], BM, min_rows);
   expected *= static_cast<long long>(nN) * (S < 1 ? 1 : S);
   if (static_cast<long long>(seen.size()) != expected)
     return printf("%zu distinct tiles assigned, %lld expected (grid %u)\n", seen.size(), expected, grid), 1;
@@ -117,9 +119,11 @@ int main() {
     const int n_cu = cus[it % 5];
     if (check<256, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
     if (check<384, true>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
+    // beside the weight-streaming kernel: only experts above 64 rows
+    if (check<256, false>(off, E, rows_bound, nN, 1, n_cu, nk, &tiles, 64)) return 1;
     // the down pass with h in two bf16 terms: 128 output rows per tile
     if (check<128, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
-    cases += 3;
+    cases += 4;
   }
   printf("ok: %d cases, %lld tiles\n", cases, tiles);
   return 0;
