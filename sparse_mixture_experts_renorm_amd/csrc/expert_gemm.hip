@@ -479,38 +479,76 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restr
   // pairs with up block nb + NBW/2.
   // With TWO, token block i < 2 of this wave is output rows (wm + 2i)*32 ..
   // and block i + 2 holds the second term of the same rows.
+  // Each 32-row block goes out through a per-wave LDS tile, as whole rows
+  // per store instruction (from the accumulator layout one instruction
+  // wrote 16 or 32 bytes into each of 32 rows). Tile rows are padded so
+  // that the LDS writes are free of bank conflicts.
+  __syncthreads();  // every wave is done reading the last stage
+  if constexpr (GATE_UP) {
+    static_assert(NBW == 2, "one gate block of 32 columns per wave");
+    constexpr int kStgH = 40;  // bf16 per tile row
+    bf16_t* stg = reinterpret_cast<bf16_t*>(lds0a) + wave * (32 * kStgH);
+    const int n = tile.nt * 128 + wn * 32 + (lane & 3) * 8;
 #pragma unroll
-  for (int mb = 0; mb < (TWO ? 2 : 4); ++mb) {
-    const int m = (wm + 2 * mb) * 32 + (lane & 31);
-    if (m >= tile.rows) continue;
-    const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
+    for (int mb = 0; mb < 4; ++mb) {
+      const int mbase = (wm + 2 * mb) * 32;
+      if (mbase >= tile.rows) continue;
+      uint32_t hi[4][2], lo[4][2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int nloc = 8 * g + 4 * half;
-      if (GATE_UP) {
+      for (int g = 0; g < 4; ++g) {
+        float hv[4];
 #pragma unroll
-        for (int nb = 0; nb < NBW / 2; ++nb) {
-          const int n = tile.nt * 128 + wn * (NBW / 2) * 32 + nb * 32 + nloc;
-          if (n < N) {
-            float hv[4];
+        for (int i = 0; i < 4; ++i) hv[i] = silu_fast(acc[0][mb][4 * g + i]) * acc[1][mb][4 * g + i];
+        hi[g][0] = pack_bf16x2(hv[0], hv[1]);
+        hi[g][1] = pack_bf16x2(hv[2], hv[3]);
+        lo[g][0] = pack_bf16x2(hv[0] - __uint_as_float(hi[g][0] << 16),
+                               hv[1] - __uint_as_float(hi[g][0] & 0xFFFF0000u));
+        lo[g][1] = pack_bf16x2(hv[2] - __uint_as_float(hi[g][1] << 16),
+                               hv[3] - __uint_as_float(hi[g][1] & 0xFFFF0000u));
+      }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              hv[i] = silu_fast(acc[nb][mb][4 * g + i]) * acc[nb + NBW / 2][mb][4 * g + i];
-            store_h(static_cast<bf16_t*>(Cv), Clo, crow + n, hv);
-          }
+      for (int term = 0; term < 2; ++term) {
+        if (term == 1 && !Clo) break;
+        bf16_t* dst = term == 0 ? static_cast<bf16_t*>(Cv) : Clo;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(stg + (lane & 31) * kStgH + 8 * g + 4 * half) =
+              term == 0 ? make_uint2(hi[g][0], hi[g][1]) : make_uint2(lo[g][0], lo[g][1]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int rr = (lane >> 2) + 16 * q, m = mbase + rr;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + rr * kStgH + (lane & 3) * 8);
+          if (m < tile.rows && n < N)
+            *reinterpret_cast<uint4*>(dst + static_cast<size_t>(tile.row0 + m) * N + n) = v;
         }
-      } else {
+      }
+    }
+  } else {
+    constexpr int kStg = 36;  // floats per tile row
+    float* stg = reinterpret_cast<float*>(wave < 4 ? lds0a : lds1a) + (wave & 3) * (32 * kStg);
+    float* Cf = static_cast<float*>(Cv) + tile.ks * c_split;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          const int n = tile.nt * TW + wn * NBW * 32 + nb * 32 + nloc;
-          if (n < N) {
-            float v[4];
+    for (int mb = 0; mb < (TWO ? 2 : 4); ++mb) {
+      const int mbase = (wm + 2 * mb) * 32;
+      if (mbase >= tile.rows) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              v[i] = TWO ? acc[nb][mb][4 * g + i] + acc[nb][mb + 2][4 * g + i] : acc[nb][mb][4 * g + i];
-            *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          }
+      for (int nb = 0; nb < NBW; ++nb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = TWO ? acc[nb][mb][4 * g + i] + acc[nb][mb + 2][4 * g + i] : acc[nb][mb][4 * g + i];
+          *reinterpret_cast<float4*>(stg + (lane & 31) * kStg + 8 * g + 4 * half) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+        const int n = tile.nt * TW + wn * NBW * 32 + nb * 32 + (lane & 7) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = (lane >> 3) + 8 * q, m = mbase + rr;
+          const float4 v = *reinterpret_cast<const float4*>(stg + rr * kStg + (lane & 7) * 4);
+          if (m < tile.rows && n < N)
+            *reinterpret_cast<float4*>(Cf + static_cast<size_t>(tile.row0 + m) * N + n) = v;
         }
       }
     }
@@ -723,15 +761,17 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
     // acc[nb][mb] element i: token row (wm + 4 mb)*32 + lane%32, weight-tile
     // row (block nb) + 8*(i/4) + 4*(lane/32) + i%4; gate block nb pairs with
     // up block nb + NB/2.
+    if constexpr (GATE_UP) {
+      // h (bf16) straight from the accumulators (through LDS, as y below,
+      // this kernel's gate/up pass ran 10-14% slower)
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-      const int m = (wm + 4 * mb) * 32 + (lane & 31);
-      if (m >= tile.rows) continue;
-      const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
+      for (int mb = 0; mb < MBW; ++mb) {
+        const int m = (wm + 4 * mb) * 32 + (lane & 31);
+        if (m >= tile.rows) continue;
+        const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nloc = 8 * g + 4 * half;
-        if (GATE_UP) {
+        for (int g = 0; g < 4; ++g) {
+          const int nloc = 8 * g + 4 * half;
 #pragma unroll
           for (int nb = 0; nb < NB / 2; ++nb) {
             const int n = n0 + wn * (WR / 4) + nb * 32 + nloc;
@@ -743,14 +783,37 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
               store_h(static_cast<bf16_t*>(Cv), Clo, crow + n, hv);
             }
           }
-        } else {
+        }
+      }
+    } else {
+      // y (fp32): each 32 x 32 block of the wave's accumulators goes through
+      // a per-wave LDS tile and out as 8 rows x 128 contiguous bytes per
+      // store instruction (stored straight from the accumulator layout, one
+      // instruction wrote 32 bytes into each of 32 rows). Rows of the tile
+      // are kStg floats apart, which keeps both LDS passes free of bank
+      // conflicts but for one 2-way group.
+      constexpr int kStg = 36;
+      __syncthreads();  // every wave is done reading the last stage
+      float* stg = reinterpret_cast<float*>(lds0a) + wave * (32 * kStg);
+      float* Cf = static_cast<float*>(Cv) + tile.ks * c_split;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int n = n0 + wn * (WR / 2) + nb * 32 + nloc;
-            if (n < N)
-              *reinterpret_cast<float4*>(static_cast<float*>(Cv) + tile.ks * c_split + crow + n) =
-                  make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
-                              acc[nb][mb][4 * g + 3]);
+      for (int mb = 0; mb < MBW; ++mb) {
+        const int mbase = (wm + 4 * mb) * 32;
+        if (mbase >= tile.rows) continue;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(stg + (lane & 31) * kStg + 8 * g + 4 * half) =
+                make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                            acc[nb][mb][4 * g + 3]);
+          const int n = n0 + wn * (WR / 2) + nb * 32 + (lane & 7) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int rr = (lane >> 3) + 8 * q, m = mbase + rr;
+            const float4 v = *reinterpret_cast<const float4*>(stg + rr * kStg + (lane & 7) * 4);
+            if (m < tile.rows && n < N)
+              *reinterpret_cast<float4*>(Cf + static_cast<size_t>(tile.row0 + m) * N + n) = v;
           }
         }
       }

@@ -182,6 +182,9 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
         if (!(e < E && col_ok)) b[u][nb] = zero;
       }
     }
+    // every load of the slices goes out before the first product (without
+    // the fence the compiler interleaves them with the products)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll

@@ -184,6 +184,10 @@ ROW_SPLITS = [
     ([384, 385, 1151, 1153], 64, 96),        # tall tiles: exactly one tile, one row more, 3 and 4 tiles
     ([257, 511, 512, 513, 31, 33], 64, 96),  # 256 x 256 tiles
     ([1, 32, 33, 800], 64, 96),              # tiny experts beside a large one
+    # tall tiles with light experts: tiles of at most 128 rows load only
+    # their first 128 token rows per step (the 129-row tile loads all 384)
+    ([5000, 100, 20, 1, 128, 129], 64, 128),
+    ([4000, 1, 65, 128, 129], 1040, 1024),   # one-term h, reduction tails
 ]
 
 
