@@ -90,7 +90,10 @@ __host__ __device__ inline void row_tile_prefix(const int32_t* __restrict__ offs
 // (-1: whole column tile; 0 or 1: that half of its weight rows)}.
 // The tile list runs over the experts in order; inside an expert over the
 // split parts, and inside a part over column tiles and, for each, over its
-// row tiles.
+// row tiles -- or, when the expert has more rows than the operation has
+// weight rows (wrows), over row tiles and, for each, over its column tiles.
+// The tiles that run side by side on an XCD then share the larger operand
+// through its L2, and the smaller one is what is read again per round.
 // With max_split > 1 the reduction dimension may be cut into S <= max_split
 // parts, each a separate tile whose partial result goes to its own output
 // slice; S is chosen from the real tile count to minimise the number of
@@ -107,7 +110,7 @@ __host__ __device__ inline void row_tile_prefix(const int32_t* __restrict__ offs
 template <int BM, bool TAIL>
 __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets, const int* pref,
                                             int E, int nN, int max_split, int n_cu, int nk,
-                                            int block, int* res) {
+                                            int wrows, int block, int* res) {
   const int base = pref[E] * nN;
   int S = 1, best_rounds = (base + n_cu - 1) / n_cu;  // rounds of S-tiles
   for (int c = 2; c <= max_split && c * kMinSplitSteps <= nk; ++c) {
@@ -157,13 +160,14 @@ __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets,
   // blocks allow (block counts differ by at most one, each at most BM/32):
   // the tiles that share a weight tile then take about the same time and
   // stay in step, and no tile is mostly padding.
-  const int mi = L % mt, nb = (m + 31) / 32;
+  const bool row_outer = m > wrows;
+  const int mi = row_outer ? L / nN : L % mt, nb = (m + 31) / 32;
   const int b0 = static_cast<int>(static_cast<long long>(mi) * nb / mt);
   const int b1 = static_cast<int>(static_cast<long long>(mi + 1) * nb / mt);
   res[0] = e;
   res[1] = offsets[e] + 32 * b0;
   res[2] = (32 * b1 < m ? 32 * b1 : m) - 32 * b0;
-  res[3] = L / mt;
+  res[3] = row_outer ? L % nN : L / mt;
   res[4] = ks;
 }
 
@@ -177,7 +181,7 @@ static_assert(kMaxExperts <= 4 * kWave, "map_tile sums four experts per lane");
 // thread 0 runs assign_tile on it. s_map: kMapLdsInts ints of LDS.
 template <int BM, bool TAIL = false>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
-                         int n_cu, int nk, int min_rows, Tile* out, int* s_map) {
+                         int n_cu, int nk, int min_rows, int wrows, Tile* out, int* s_map) {
   int* pref = s_map + 8;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
@@ -204,7 +208,8 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int
     if (lane == kWave - 1) pref[E] = incl;
   }
   __syncthreads();
-  if (threadIdx.x == 0) assign_tile<BM, TAIL>(offsets, pref, E, nN, max_split, n_cu, nk, blockIdx.x, s_map);
+  if (threadIdx.x == 0)
+    assign_tile<BM, TAIL>(offsets, pref, E, nN, max_split, n_cu, nk, wrows, blockIdx.x, s_map);
   __syncthreads();
   out->S = s_map[5];
   if (s_map[0] < 0) return false;
@@ -291,7 +296,8 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restr
   Tile tile;
   const int nk = (K + TK - 1) / TK;
   __shared__ int s_map[kMapLdsInts];
-  const bool have = map_tile<BM>(offsets, E, nN, max_split, n_cu, nk, min_rows, &tile, s_map);
+  const bool have = map_tile<BM>(offsets, E, nN, max_split, n_cu, nk, min_rows, GATE_UP ? 2 * N : N,
+                                 &tile, s_map);
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;
   // reduction steps [kbeg, kend) of this tile
@@ -593,8 +599,8 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const int nN = GATE_UP ? (N + 127) / 128 : (N + TW - 1) / TW;
   Tile tile;
   const int nk = (K + TK - 1) / TK;
-  const bool have = map_tile<TM3, true>(offsets, E, nN, max_split, n_cu, nk, min_rows, &tile,
-                                        reinterpret_cast<int*>(lds1a));
+  const bool have = map_tile<TM3, true>(offsets, E, nN, max_split, n_cu, nk, min_rows,
+                                        GATE_UP ? 2 * N : N, &tile, reinterpret_cast<int*>(lds1a));
   __syncthreads();
   if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
   if (!have) return;

@@ -18,7 +18,7 @@ using namespace moe;
 
 template <int BM, bool TAIL>
 static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN, int max_split,
-                 int n_cu, int nk, long long* tiles_seen, int min_rows = 0) {
+                 int n_cu, int nk, long long* tiles_seen, int min_rows = 0, int wrows = 1 << 30) {
   const unsigned grid = TAIL ? tall_grid(rows_bound, E, nN, max_split, n_cu)
                              : tile_grid(rows_bound, E, BM, nN, max_split);
   // key (e, row tile, column tile, part) -> counts {whole, half 0, half 1}
@@ -30,7 +30,8 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
   row_tile_prefix<BM>(off.data(), E, pref.data(), min_rows);
   for (unsigned b = 0; b < grid; ++b) {
     int res[7];
-    assign_tile<BM, TAIL>(off.data(), pref.data(), E, nN, max_split, n_cu, nk, static_cast<int>(b), res);
+    assign_tile<BM, TAIL>(off.data(), pref.data(), E, nN, max_split, n_cu, nk, wrows,
+                          static_cast<int>(b), res);
     if (S < 0) S = res[5];
     if (res[5] != S) return printf("split count differs between workgroups\n"), 1;
     if (res[0] < 0) continue;
@@ -117,8 +118,11 @@ int main() {
     const int max_split = (it & 1) ? kMaxDownSplit : 1;
     const int nk = 1 + static_cast<int>(rng() % 400);
     const int n_cu = cus[it % 5];
-    if (check<256, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
-    if (check<384, true>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
+    // the order inside an expert follows its row count against the weight
+    // rows: all column-major, all row-major, or mixed
+    const int wrows = (it % 3 == 0) ? 1 << 30 : (it % 3 == 1 ? 0 : 64 + static_cast<int>(rng() % 2000));
+    if (check<256, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles, 0, wrows)) return 1;
+    if (check<384, true>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles, 0, wrows)) return 1;
     // beside the weight-streaming kernel: only experts above 64 rows
     if (check<256, false>(off, E, rows_bound, nN, 1, n_cu, nk, &tiles, 64)) return 1;
     // the down pass with h in two bf16 terms: 128 output rows per tile
