@@ -60,9 +60,13 @@ def test_route_logits_bitexact(M, kind, T, E, k):
 
 
 @pytest.mark.parametrize("kind", wl.ROUTING_KINDS)
-@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (513, 8, 2), (2048, 8, 2), (3000, 64, 8),
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (513, 8, 2), (3000, 64, 8),
                                    (100, 256, 16), (700, 6, 3), (5000, 1, 1), (8192, 64, 8),
-                                   (70000, 8, 2), (300000, 4, 1)])
+                                   (70000, 8, 2), (300000, 4, 1),
+                                   # around the one-pass kernel's limits (4096
+                                   # assignments, 64 experts)
+                                   (2048, 8, 2), (2049, 8, 2), (512, 64, 8), (500, 65, 8),
+                                   (100, 32, 16)])
 def test_permute_bitexact(M, kind, T, E, k):
     if kind == "even_only" and 2 * k > E:
         pytest.skip("needs 2k <= E")
