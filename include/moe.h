@@ -40,7 +40,9 @@
  *   - Results are deterministic: no floating-point atomics are used, so two
  *     calls on the same inputs give bit-identical outputs.
  *   - Precision, MOE_BF16: bf16 operands on the bf16 MFMA with fp32
- *     accumulation, SiLU in fp32, expert outputs and the combine in fp32.
+ *     accumulation, SiLU in fp32, each expert output kept to 16 significant
+ *     bits (relative error at most 2^-16) until the combine, which sums in
+ *     fp32.
  *     The hidden activation h = SiLU(gate) * up is the down projection's
  *     MFMA operand, so it is carried in bf16: when d >= 1024 and
  *     ffn >= 1024 as one term (its rounding to nearest even), otherwise as
@@ -86,8 +88,9 @@ const char* moe_status_string(moe_status s);
  * shape: routing results, per-expert offsets, the permutation, the hidden
  * activations h [T*k, ffn] (in dt; twice that for a bf16 layer narrower than
  * 1024 in d or ffn, whose h takes two bf16 terms) and expert outputs
- * y [T*k, d] (fp32, up to four partial sums). Returns 0 for invalid or
- * unsupported shapes. Host-only; no device access. */
+ * y [T*k, d] (up to four partial sums; 3 bytes per element for bf16 layers,
+ * 4 for fp32). Returns 0 for invalid or unsupported shapes. Host-only; no
+ * device access. */
 size_t moe_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt);
 
 /* Router projection + softmax + top-k + renormalisation (one kernel).
@@ -187,7 +190,7 @@ moe_status moe_forward_profiled(const void* x, const void* w_router, const void*
  * Limit: shapes whose moe_workspace_size(T, d, ffn, E, k, dt) exceeds
  * MOE_NO_ALLOC_SCRATCH_BYTES return MOE_WORKSPACE_TOO_SMALL and enqueue
  * nothing (at the Mixtral widths d = 4096, ffn = 14336, E = 8, k = 2 that
- * is T above 356 tokens: decode-sized batches fit). The first call on a
+ * is T above 431 tokens: decode-sized batches fit). The first call on a
  * device looks up that device's copy of the array (MOE_HIP_ERROR if the
  * lookup fails). Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race and give undefined

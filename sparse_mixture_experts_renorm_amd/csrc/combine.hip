@@ -7,11 +7,12 @@
 // atomics are needed; the k terms are added in slot order (j = 0..k-1) in
 // fp32, which fixes the rounding independently of scheduling.
 //
-// y is fp32 and may hold S partial sums of the down GEMM's reduction (S is
-// read from the device, where the down GEMM chose it); each expert row is
-// the sum of its S parts in part order, then weighted. Each thread owns 8
-// consecutive columns of one token (two 16-byte loads per term); a
-// workgroup covers 2048 columns.
+// y holds S partial sums of the down GEMM's reduction (S is read from the
+// device, where the down GEMM chose it), fp32 for an fp32 layer and in the
+// 24-bit format of common.h for a bf16 layer; each expert row is the sum of
+// its S parts in part order, then weighted. Each thread owns 8 consecutive
+// columns of one token (32 or 24 bytes per term); a workgroup covers 2048
+// columns.
 //
 // Block options (the extended forward): after the k routed terms come the
 // outputs of the shared experts, each with weight 1 and in expert order
@@ -32,6 +33,25 @@ __device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// eight 24-bit values (24 bytes, 8-byte aligned: the column is a multiple
+// of 8)
+__device__ __forceinline__ void load8_f24(const char* p, float v[8]) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  const uint2 b = *reinterpret_cast<const uint2*>(p + 8);
+  const uint2 c = *reinterpret_cast<const uint2*>(p + 16);
+  unpack_f24x4(a.x, a.y, b.x, v);
+  unpack_f24x4(b.y, c.x, c.y, v + 4);
+}
+
+// row r, columns col.. of y (element index r*d + col), in the format F24
+template <bool F24>
+__device__ __forceinline__ void load_y(const void* y, size_t at, float v[8]) {
+  if constexpr (F24)
+    load8_f24(static_cast<const char*>(y) + at * 3, v);
+  else
+    load8<float>(static_cast<const float*>(y) + at, v);
 }
 
 template <>
@@ -61,16 +81,17 @@ __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float v[8]) {
 }
 
 struct CombineExtra {
-  const float* ys;          // shared experts' outputs: parts of [n_shared * T, d], or null
+  const void* ys;           // shared experts' outputs: parts of [n_shared * T, d], or null
   const int32_t* ys_split;  // number of parts in ys
   size_t ys_stride;         // elements between parts
   int n_shared, T;
   const void* resid;        // residual input [T, d] (fp32 or bf16), or null
 };
 
-// RES: 0 no residual, 1 fp32 residual, 2 bf16 residual; SH: shared experts.
-template <typename OT, int RES, bool SH>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+// RES: 0 no residual, 1 fp32 residual, 2 bf16 residual; SH: shared experts;
+// F24: y and ys in the 24-bit format.
+template <typename OT, int RES, bool SH, bool F24>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ split,
                                                       size_t split_stride,
                                                       const int32_t* __restrict__ inv_pos,
@@ -85,12 +106,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int p = inv_pos[static_cast<size_t>(t) * k + j];
     if (p < 0) continue;
     const float wj = w[static_cast<size_t>(t) * k + j];
-    const float* yp = y + static_cast<size_t>(p) * d + col;
+    const size_t at = static_cast<size_t>(p) * d + col;
     float v[8];
-    load8<float>(yp, v);
+    load_y<F24>(y, at, v);
     for (int s = 1; s < S; ++s) {
       float u[8];
-      load8<float>(yp + s * split_stride, u);
+      load_y<F24>(y, at + s * split_stride, u);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] += u[i];
     }
@@ -100,12 +121,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if constexpr (SH) {
     const int Ss = *ex.ys_split;
     for (int sh = 0; sh < ex.n_shared; ++sh) {
-      const float* yp = ex.ys + (static_cast<size_t>(sh) * ex.T + t) * d + col;
+      const size_t at = (static_cast<size_t>(sh) * ex.T + t) * d + col;
       float v[8];
-      load8<float>(yp, v);
+      load_y<F24>(ex.ys, at, v);
       for (int s = 1; s < Ss; ++s) {
         float u[8];
-        load8<float>(yp + s * ex.ys_stride, u);
+        load_y<F24>(ex.ys, at + s * ex.ys_stride, u);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] += u[i];
       }
@@ -125,52 +146,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   store8<OT>(out + static_cast<size_t>(t) * d + col, acc);
 }
 
-template <typename OT, int RES, bool SH>
-void combine_launch(dim3 grid, hipStream_t s, const float* y, const int32_t* split, size_t stride,
+template <typename OT, int RES, bool SH, bool F24>
+void combine_launch(dim3 grid, hipStream_t s, const void* y, const int32_t* split, size_t stride,
                     const int32_t* inv_pos, const float* w, int d, int k, const CombineExtra& ex,
                     void* out) {
-  combine_kernel<OT, RES, SH><<<grid, 256, 0, s>>>(y, split, stride, inv_pos, w, d, k, ex,
-                                                   static_cast<OT*>(out));
+  combine_kernel<OT, RES, SH, F24><<<grid, 256, 0, s>>>(y, split, stride, inv_pos, w, d, k, ex,
+                                                        static_cast<OT*>(out));
 }
 
-template <typename OT>
-void combine_dispatch(dim3 grid, hipStream_t s, const float* y, const int32_t* split,
+template <typename OT, bool F24>
+void combine_dispatch(dim3 grid, hipStream_t s, const void* y, const int32_t* split,
                       size_t stride, const int32_t* inv_pos, const float* w, int d, int k,
                       const CombineExtra& ex, int res, void* out) {
   const bool sh = ex.n_shared > 0;
   if (res == 0) {
-    if (sh) combine_launch<OT, 0, true>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
-    else combine_launch<OT, 0, false>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    if (sh) combine_launch<OT, 0, true, F24>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    else combine_launch<OT, 0, false, F24>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
   } else if (res == 1) {
-    if (sh) combine_launch<OT, 1, true>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
-    else combine_launch<OT, 1, false>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    if (sh) combine_launch<OT, 1, true, F24>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    else combine_launch<OT, 1, false, F24>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
   } else {
-    if (sh) combine_launch<OT, 2, true>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
-    else combine_launch<OT, 2, false>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    if (sh) combine_launch<OT, 2, true, F24>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
+    else combine_launch<OT, 2, false, F24>(grid, s, y, split, stride, inv_pos, w, d, k, ex, out);
   }
 }
 
 }  // namespace
 
-moe_status launch_combine_ext(const float* y, const int32_t* split, const int32_t* inv_pos,
-                              const float* topk_w, int T, int d, int k, const float* ys,
-                              const int32_t* ys_split, int n_shared, const void* resid,
-                              moe_dtype resid_dt, void* out, moe_dtype out_dt, hipStream_t s) {
+moe_status launch_combine_ext(const void* y, const int32_t* split, const int32_t* inv_pos,
+                              const float* topk_w, int T, int d, int k, moe_dtype dt,
+                              const void* ys, const int32_t* ys_split, int n_shared,
+                              const void* resid, moe_dtype resid_dt, void* out, moe_dtype out_dt,
+                              hipStream_t s) {
   dim3 grid(T, (d + 2047) / 2048);
   const size_t stride = static_cast<size_t>(T) * k * d;
   CombineExtra ex{ys, ys_split, static_cast<size_t>(T) * n_shared * d, n_shared, T, resid};
   const int res = resid == nullptr ? 0 : (resid_dt == MOE_F32 ? 1 : 2);
-  if (out_dt == MOE_F32)
-    combine_dispatch<float>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
-  else
-    combine_dispatch<bf16_t>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
+  const bool f24 = dt == MOE_BF16;
+  if (out_dt == MOE_F32) {
+    if (f24) combine_dispatch<float, true>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
+    else combine_dispatch<float, false>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
+  } else {
+    if (f24) combine_dispatch<bf16_t, true>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
+    else combine_dispatch<bf16_t, false>(grid, s, y, split, stride, inv_pos, topk_w, d, k, ex, res, out);
+  }
   return launch_status();
 }
 
-moe_status launch_combine(const float* y, const int32_t* split, const int32_t* inv_pos,
-                          const float* topk_w, int T, int d, int k, void* out, moe_dtype out_dt,
-                          hipStream_t s) {
-  return launch_combine_ext(y, split, inv_pos, topk_w, T, d, k, nullptr, nullptr, 0, nullptr,
+moe_status launch_combine(const void* y, const int32_t* split, const int32_t* inv_pos,
+                          const float* topk_w, int T, int d, int k, moe_dtype dt, void* out,
+                          moe_dtype out_dt, hipStream_t s) {
+  return launch_combine_ext(y, split, inv_pos, topk_w, T, d, k, dt, nullptr, nullptr, 0, nullptr,
                             MOE_F32, out, out_dt, s);
 }
 

@@ -54,6 +54,30 @@ __device__ __forceinline__ void store_h(bf16_t* __restrict__ hi, bf16_t* __restr
   }
 }
 
+// Expert outputs y of a bf16 layer, between the down GEMM and the combine:
+// each fp32 value rounded to its top 24 bits (sign, exponent and 15 mantissa
+// bits, nearest with ties to even), four values in three 32-bit words. The
+// relative error is at most 2^-16 (rounding h to bf16 allows 2^-8), and y's
+// stores and the combine's reads move a quarter fewer bytes. fp32 layers
+// keep fp32 y. Inputs are finite.
+__host__ __device__ __forceinline__ uint32_t f32_to_f24(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__host__ __device__ __forceinline__ uint3 pack_f24x4(float a, float b, float c, float d) {
+  const uint32_t x = f32_to_f24(a), y = f32_to_f24(b), z = f32_to_f24(c), w = f32_to_f24(d);
+  return make_uint3(x | (y << 24), (y >> 8) | (z << 16), (z >> 16) | (w << 8));
+}
+__host__ __device__ __forceinline__ void unpack_f24x4(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                     float v[4]) {
+  v[0] = __builtin_bit_cast(float, w0 << 8);
+  v[1] = __builtin_bit_cast(float, ((w0 >> 24) | (w1 << 8)) << 8);
+  v[2] = __builtin_bit_cast(float, ((w1 >> 16) | (w2 << 16)) << 8);
+  v[3] = __builtin_bit_cast(float, w2 & 0xFFFFFF00u);
+}
+// bytes per element of y for a layer of storage dtype dt
+inline size_t y_bytes(moe_dtype dt) { return dt == MOE_BF16 ? 3 : 4; }
+
 // SiLU(z) = z * sigmoid(z), in fp32.
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -97,7 +121,7 @@ struct Workspace {
   int32_t* inv_pos;       // [T*k]
   void* h;                // [T*k, ffn] in dt
   void* h_lo;             // [T*k, ffn] bf16: second term of h (two_term_h), else null
-  float* y;               // [kMaxDownSplit, T*k, d] fp32 partial sums of the down GEMM
+  void* y;                // [kMaxDownSplit, T*k, d] partial sums of the down GEMM (y_bytes(dt) each)
   int32_t* split;         // [1] number of partial sums in y
   int32_t* block_counts;  // [kPermMaxBlocks * E] per-block expert histograms of the permutation
   size_t bytes;
@@ -120,7 +144,7 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   w.inv_pos = reinterpret_cast<int32_t*>(take(tk * 4));
   w.h = take(tk * static_cast<size_t>(ffn) * es);
   w.h_lo = two_term_h(d, ffn, dt) ? take(tk * static_cast<size_t>(ffn) * es) : nullptr;
-  w.y = reinterpret_cast<float*>(take(kMaxDownSplit * tk * static_cast<size_t>(d) * 4));
+  w.y = take(kMaxDownSplit * tk * static_cast<size_t>(d) * y_bytes(dt));
   w.split = reinterpret_cast<int32_t*>(take(4));
   w.block_counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(kPermMaxBlocks) * E * 4));
   w.bytes = off;
@@ -135,7 +159,7 @@ struct ExtWorkspace {
   int32_t* off_s;         // [n_shared+1]
   void* h_s;              // [n_shared*T, shared_ffn] in dt
   void* h_s_lo;           // second term of h_s (two_term_h for shared_ffn), else null
-  float* y_s;             // [kMaxDownSplit, n_shared*T, d] fp32
+  void* y_s;              // [kMaxDownSplit, n_shared*T, d] (y_bytes(dt) each)
   int32_t* split_s;       // [1]
   size_t bytes;
 };
@@ -156,7 +180,7 @@ inline ExtWorkspace carve_ext_workspace(void* base, int T, int d, int ffn, int E
     w.h_s = take(ts * static_cast<size_t>(shared_ffn) * es);
     w.h_s_lo = two_term_h(d, shared_ffn, dt) ? take(ts * static_cast<size_t>(shared_ffn) * es)
                                              : nullptr;
-    w.y_s = reinterpret_cast<float*>(take(kMaxDownSplit * ts * static_cast<size_t>(d) * 4));
+    w.y_s = take(kMaxDownSplit * ts * static_cast<size_t>(d) * y_bytes(dt));
     w.split_s = reinterpret_cast<int32_t*>(take(4));
   }
   w.bytes = off;
@@ -191,7 +215,7 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
                           int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s);
 moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
-                       int T, int d, int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
+                       int T, int d, int ffn, int E, int k, moe_dtype dt, void* y, int32_t* split,
                        hipStream_t s);
 // Weight-streaming kernels; experts with more than max_rows rows are skipped
 // (left to a tiled launch). The down pass cuts its reduction into at most
@@ -201,7 +225,7 @@ moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  int d, int ffn, int E, int rows, void* h, bf16_t* h_lo,
                                  int max_rows, hipStream_t s);
 moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* offsets,
-                              const void* w_down, int d, int ffn, int E, int rows, float* y,
+                              const void* w_down, int d, int ffn, int E, int rows, void* y,
                               int32_t* split, int max_rows, int max_split, hipStream_t s);
 // Few rows per expert: the weight-streaming kernels replace the tiled ones.
 inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
@@ -211,13 +235,14 @@ int router_stats_blocks(int T);
 moe_status launch_router_stats(const float* probs, const int32_t* counts, int T, int E,
                                float* mean_probs, float* frac, float* loss, float* partial,
                                hipStream_t s);
-moe_status launch_combine(const float* y, const int32_t* split, const int32_t* inv_pos,
-                          const float* topk_w, int T, int d, int k, void* out, moe_dtype out_dt,
-                          hipStream_t s);
+// y (and ys) in the format of a layer of dtype dt: 24-bit for bf16, fp32.
+moe_status launch_combine(const void* y, const int32_t* split, const int32_t* inv_pos,
+                          const float* topk_w, int T, int d, int k, moe_dtype dt, void* out,
+                          moe_dtype out_dt, hipStream_t s);
 // ys: outputs of n_shared shared experts (their own split count ys_split);
 // resid: [T, d] in resid_dt added last; both optional.
-moe_status launch_combine_ext(const float* y, const int32_t* split, const int32_t* inv_pos,
-                              const float* topk_w, int T, int d, int k, const float* ys,
+moe_status launch_combine_ext(const void* y, const int32_t* split, const int32_t* inv_pos,
+                              const float* topk_w, int T, int d, int k, moe_dtype dt, const void* ys,
                               const int32_t* ys_split, int n_shared, const void* resid,
                               moe_dtype resid_dt, void* out, moe_dtype out_dt, hipStream_t s);
 

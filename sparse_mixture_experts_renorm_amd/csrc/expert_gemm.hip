@@ -6,9 +6,10 @@
 // X_e are the rows sorted_token[offsets[e] .. offsets[e+1]) of x: the gather
 // is done by the tile loads, so X_e is never written out. h and y are stored
 // in permuted-row order, row offsets[e] + r for the r-th token of expert e.
-// h is bf16 (the down pass multiplies it on the bf16 MFMA); y stays fp32,
-// because rounding y to bf16 as well would spend about half of the 2e-2 x RMS
-// error budget of bf16 workloads on top of h's rounding.
+// h is bf16 (the down pass multiplies it on the bf16 MFMA); y keeps 16
+// significant bits (the 24-bit format of common.h), because rounding y to
+// bf16 as well would spend about half of the 2e-2 x RMS error budget of bf16
+// workloads on top of h's rounding.
 //
 // bf16 path (gfx950), two tile shapes: 256 x 256 (below) and the tall
 // 384 x 256 tiles further down, taken when the experts average at least 768
@@ -255,7 +256,7 @@ constexpr int TK = 64;         // reduction step (elements); one LDS row = 128 b
 constexpr int STAGE = TM * TK * 2;  // bytes per operand and stage (32 KB)
 
 // GATE_UP: A = x gathered by sorted_token, weights = [w_gate; w_up], C = h (bf16).
-// !GATE_UP: A = h (rows in order), weights = w_down, C = y (fp32); the
+// !GATE_UP: A = h (rows in order), weights = w_down, C = y (24-bit); the
 // reduction may be split (see assign_tile): part ks writes C + ks * c_split,
 // and workgroup 0 stores the split count S in *split_out.
 // NW waves per workgroup: 4 (wave tile 128 x 128, one wave per SIMD) or 8
@@ -532,7 +533,7 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restr
   } else {
     constexpr int kStg = 36;  // floats per tile row
     float* stg = reinterpret_cast<float*>(wave < 4 ? lds0a : lds1a) + (wave & 3) * (32 * kStg);
-    float* Cf = static_cast<float*>(Cv) + tile.ks * c_split;
+    char* Cb = static_cast<char*>(Cv) + tile.ks * c_split * 3;  // 24-bit y
 #pragma unroll
     for (int mb = 0; mb < (TWO ? 2 : 4); ++mb) {
       const int mbase = (wm + 2 * mb) * 32;
@@ -554,7 +555,8 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restr
           const int rr = (lane >> 3) + 8 * q, m = mbase + rr;
           const float4 v = *reinterpret_cast<const float4*>(stg + rr * kStg + (lane & 7) * 4);
           if (m < tile.rows && n < N)
-            *reinterpret_cast<float4*>(Cf + static_cast<size_t>(tile.row0 + m) * N + n) = v;
+            *reinterpret_cast<uint3*>(Cb + (static_cast<size_t>(tile.row0 + m) * N + n) * 3) =
+                pack_f24x4(v.x, v.y, v.z, v.w);
         }
       }
     }
@@ -792,16 +794,16 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
         }
       }
     } else {
-      // y (fp32): each 32 x 32 block of the wave's accumulators goes through
-      // a per-wave LDS tile and out as 8 rows x 128 contiguous bytes per
-      // store instruction (stored straight from the accumulator layout, one
-      // instruction wrote 32 bytes into each of 32 rows). Rows of the tile
+      // y (24-bit format): each 32 x 32 block of the wave's accumulators goes
+      // through a per-wave LDS tile and out as 8 rows x 96 contiguous bytes
+      // per store instruction (stored straight from the accumulator layout,
+      // one instruction wrote 32 bytes into each of 32 rows). Rows of the tile
       // are kStg floats apart, which keeps both LDS passes free of bank
       // conflicts but for one 2-way group.
       constexpr int kStg = 36;
       __syncthreads();  // every wave is done reading the last stage
       float* stg = reinterpret_cast<float*>(lds0a) + wave * (32 * kStg);
-      float* Cf = static_cast<float*>(Cv) + tile.ks * c_split;
+      char* Cb = static_cast<char*>(Cv) + tile.ks * c_split * 3;  // 24-bit y
 #pragma unroll
       for (int mb = 0; mb < MBW; ++mb) {
         const int mbase = (wm + 4 * mb) * 32;
@@ -819,7 +821,8 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
             const int rr = (lane >> 3) + 8 * q, m = mbase + rr;
             const float4 v = *reinterpret_cast<const float4*>(stg + rr * kStg + (lane & 7) * 4);
             if (m < tile.rows && n < N)
-              *reinterpret_cast<float4*>(Cf + static_cast<size_t>(tile.row0 + m) * N + n) = v;
+              *reinterpret_cast<uint3*>(Cb + (static_cast<size_t>(tile.row0 + m) * N + n) * 3) =
+                  pack_f24x4(v.x, v.y, v.z, v.w);
           }
         }
       }
@@ -959,13 +962,13 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
 }
 
 moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
-                       int T, int d, int ffn, int E, int k, moe_dtype dt, float* y, int32_t* split,
+                       int T, int d, int ffn, int E, int k, moe_dtype dt, void* y, int32_t* split,
                        hipStream_t s) {
   const int rows = T * k;
   if (dt == MOE_F32) {
     expert_gemm_f32_kernel<false><<<dim3(rows, (d + 255) / 256), 256, 0, s>>>(
         static_cast<const float*>(h), nullptr, offsets, E, static_cast<const float*>(w_down),
-        nullptr, d, ffn, y, split);
+        nullptr, d, ffn, static_cast<float*>(y), split);
     return launch_status();
   }
   const bf16_t* hb = static_cast<const bf16_t*>(h);

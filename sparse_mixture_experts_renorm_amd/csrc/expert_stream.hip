@@ -19,7 +19,8 @@
 //   - weights go straight from memory to registers, DEPTH 64-wide reduction
 //     chunks ahead;
 //   - the down GEMM may cut the reduction into S parts (blockIdx.z), each
-//     writing its own fp32 partial; the combine sums the parts in order;
+//     writing its own partial (24-bit format); the combine sums the parts in
+//     order;
 //   - experts without rows exit at once, so their weights are never read;
 //     so do experts with more than max_rows rows, which a tiled launch takes
 //     (their weights would otherwise be read once per 16*NB rows).
@@ -186,8 +187,8 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
         for (int i = 0; i < 4; ++i) hv[i] = silu_fast(accg[r][t][i]) * accu[r][t][i];
         store_h(static_cast<bf16_t*>(Cv), Clo, crow + n, hv);
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(Cv) + crow + n) =
-            make_float4(accg[r][t][0], accg[r][t][1], accg[r][t][2], accg[r][t][3]);
+        *reinterpret_cast<uint3*>(static_cast<char*>(Cv) + (crow + n) * 3) =
+            pack_f24x4(accg[r][t][0], accg[r][t][1], accg[r][t][2], accg[r][t][3]);
       }
     }
   }
@@ -196,8 +197,8 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
 // Grid: (ceil(N / (16 * RB * SW)), E, S). GATE_UP: A = x gathered by
 // sorted_token, weight rows from w_gate and w_up, C = h (bf16; with Clo
 // non-null its second term goes there). !GATE_UP: A = h rows (TWO: plus
-// their second terms Alo), weights w_down, C = y (fp32), part z at
-// C + z * c_split.
+// their second terms Alo), weights w_down, C = y (24-bit format), part z at
+// element z * c_split.
 template <bool GATE_UP, int RB, int NB, bool TWO = false>
 __global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ Alo,
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
     wg[r] = B0 + wrow;
     wu[r] = GATE_UP ? B1 + wrow : nullptr;
   }
-  void* C = GATE_UP ? Cv : static_cast<void*>(static_cast<float*>(Cv) + z * c_split);
+  void* C = GATE_UP ? Cv : static_cast<void*>(static_cast<char*>(Cv) + z * c_split * 3);
   for (int mb = 0; mb < rows; mb += 16 * NB)
     stream_pass<GATE_UP, RB, NB, TWO>(A, Alo, sorted_token, wg, wu, row0, rows, mb, n0, N, K,
                                       kbeg, kend, C, Clo, lane);
@@ -262,7 +263,7 @@ moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
 }
 
 moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* offsets,
-                              const void* w_down, int d, int ffn, int E, int rows, float* y,
+                              const void* w_down, int d, int ffn, int E, int rows, void* y,
                               int32_t* split, int max_rows, int max_split, hipStream_t s) {
   constexpr int RB = kRbDown;
   // cut the reduction (into whole 64-wide chunks, at least 16 per part)

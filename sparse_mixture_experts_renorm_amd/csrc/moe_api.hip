@@ -214,7 +214,7 @@ static moe_status run_experts(const void* x, const int32_t* topk_idx, const floa
                    stream);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[4], stream);
-  st = launch_combine(ws.y, ws.split, ws.inv_pos, topk_w, T, d, k, out, out_dt, stream);
+  st = launch_combine(ws.y, ws.split, ws.inv_pos, topk_w, T, d, k, dt, out, out_dt, stream);
   if (ev) hipEventRecord(ev[5], stream);
   return st;
 }
@@ -356,7 +356,7 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
                      w.y_s, w.split_s, stream);
     if (st != MOE_OK) return st;
   }
-  return launch_combine_ext(b.y, b.split, b.inv_pos, b.topk_w, T, d, k, w.y_s, w.split_s, S,
+  return launch_combine_ext(b.y, b.split, b.inv_pos, b.topk_w, T, d, k, dt, w.y_s, w.split_s, S,
                             opt->residual ? x : nullptr, dt, out, out_dt, stream);
 }
 

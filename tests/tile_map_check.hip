@@ -7,7 +7,9 @@
 #include "../sparse_mixture_experts_renorm_amd/csrc/expert_gemm.hip"
 #include "../sparse_mixture_experts_renorm_amd/csrc/expert_stream.hip"
 
+#include <cmath>
 #include <cstdio>
+#include <cstring>
 #include <algorithm>
 #include <map>
 #include <random>
@@ -94,7 +96,38 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
   return 0;
 }
 
+// The 24-bit format of y (common.h): four values through three words and
+// back are each the value rounded to 16 significant bits, nearest with ties
+// to even, i.e. within 2^-16 of it relative, and exact when the low 8 bits
+// are zero.
+static int check_f24() {
+  std::mt19937 rng(7);
+  std::normal_distribution<float> nd(0.f, 1.f);
+  for (int it = 0; it < 200000; ++it) {
+    float v[4], back[4];
+    for (int i = 0; i < 4; ++i) v[i] = nd(rng) * std::ldexp(1.f, static_cast<int>(rng() % 60) - 30);
+    if (it % 7 == 0) v[it % 4] = 0.f;
+    if (it % 11 == 0) v[1] = -v[1];
+    const uint3 w = pack_f24x4(v[0], v[1], v[2], v[3]);
+    unpack_f24x4(w.x, w.y, w.z, back);
+    for (int i = 0; i < 4; ++i) {
+      uint32_t u;
+      std::memcpy(&u, &v[i], 4);
+      const uint32_t low = u & 0xFFu, keep = u >> 8;
+      const uint32_t want = (low > 0x80u || (low == 0x80u && (keep & 1u))) ? (keep + 1) << 8 : keep << 8;
+      uint32_t got;
+      std::memcpy(&got, &back[i], 4);
+      if (got != want)
+        return printf("24-bit y: %a packed to %08x, want %08x\n", v[i], got, want), 1;
+      if (std::fabs(back[i] - v[i]) > std::ldexp(std::fabs(v[i]), -16))
+        return printf("24-bit y: %a off by more than 2^-16\n", v[i]), 1;
+    }
+  }
+  return 0;
+}
+
 int main() {
+  if (check_f24()) return 1;
   std::mt19937 rng(12345);
   long long tiles = 0;
   int cases = 0;
