@@ -53,7 +53,8 @@
  *     N(0,1) inputs and N(0, 0.02^2) weights, the largest error of any output
  *     element was 1.0e-2 x output RMS at the Mixtral shape, 1.4e-2 at d=2048,
  *     ffn=1408, and at most 1.6e-2 over random shapes with both widths in
- *     1024..2048; with two terms it stays below 1e-4 x RMS. Narrower layers
+ *     1024..2048; with two terms, at most 1.5e-4 x RMS over random narrow
+ *     shapes (the 16-bit expert outputs dominate there). Narrower layers
  *     with one term reached 4e-2 x RMS, which is why they take two.
  *   - Precision, MOE_F32: fp32 throughout (within 1e-4 x RMS of the exact
  *     layer). The fp32 expert kernels are a small-shape parity path: one

@@ -583,6 +583,29 @@ constexpr int STAGE_A3 = TM3 * TK * 2;  // 48 KB
 constexpr int NW3 = 8;
 constexpr int MBW = 3;                // 32-row token blocks per wave
 
+// Stores 32 columns (from n) of one row of h, held as an MFMA 32x32 block's
+// accumulator layout: lane l has columns 8g + 4(l/32) + 0..3 of each group
+// g as two packed bf16 pairs in w[g]. Lanes l and l^32 (same row) swap a
+// group each (ds_bpermute, no LDS memory), so that each lane stores 8 whole
+// columns: 16 contiguous bytes per lane and 32 per row pair of stores.
+__device__ __forceinline__ void store_h_pairs(bf16_t* __restrict__ dst, size_t crow, int n, int N,
+                                              bool ok, int half, int partner,
+                                              const uint32_t w[4][2]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int g0 = 2 * p, g1 = 2 * p + 1;
+    // the lower half keeps group g0 and takes its partner's share of g0;
+    // the upper half keeps g1
+    const uint32_t s0 = half ? w[g0][0] : w[g1][0], s1 = half ? w[g0][1] : w[g1][1];
+    const uint32_t r0 = __builtin_amdgcn_ds_bpermute(partner, static_cast<int>(s0));
+    const uint32_t r1 = __builtin_amdgcn_ds_bpermute(partner, static_cast<int>(s1));
+    const uint4 v = half ? make_uint4(r0, r1, w[g1][0], w[g1][1])
+                         : make_uint4(w[g0][0], w[g0][1], r0, r1);
+    const int c = n + 8 * (half ? g1 : g0);
+    if (ok && c < N) *reinterpret_cast<uint4*>(dst + crow + c) = v;
+  }
+}
+
 template <bool GATE_UP, bool KMASK>
 __global__ __launch_bounds__(NW3 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ sorted_token,
@@ -770,26 +793,40 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
     // row (block nb) + 8*(i/4) + 4*(lane/32) + i%4; gate block nb pairs with
     // up block nb + NB/2.
     if constexpr (GATE_UP) {
-      // h (bf16) straight from the accumulators (through LDS, as y below,
-      // this kernel's gate/up pass ran 10-14% slower)
+      // h (bf16): lanes l and l^32 hold the two halves of 8 columns of one
+      // row; one exchange between them (ds_bpermute, no LDS memory) gives
+      // each lane 8 whole columns, so each store instruction writes 32
+      // contiguous bytes into each of 32 rows, in half as many stores.
+      const int partner = (lane ^ 32) << 2;
 #pragma unroll
       for (int mb = 0; mb < MBW; ++mb) {
         const int m = (wm + 4 * mb) * 32 + (lane & 31);
-        if (m >= tile.rows) continue;
         const size_t crow = static_cast<size_t>(tile.row0 + m) * N;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int nloc = 8 * g + 4 * half;
+        for (int nb = 0; nb < NB / 2; ++nb) {
+          float hv[4][4];
+          uint32_t w[4][2];
 #pragma unroll
-          for (int nb = 0; nb < NB / 2; ++nb) {
-            const int n = n0 + wn * (WR / 4) + nb * 32 + nloc;
-            if (n < N) {
-              float hv[4];
+          for (int g = 0; g < 4; ++g) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                hv[i] = silu_fast(acc[nb][mb][4 * g + i]) * acc[nb + NB / 2][mb][4 * g + i];
-              store_h(static_cast<bf16_t*>(Cv), Clo, crow + n, hv);
+            for (int i = 0; i < 4; ++i)
+              hv[g][i] = silu_fast(acc[nb][mb][4 * g + i]) * acc[nb + NB / 2][mb][4 * g + i];
+            w[g][0] = pack_bf16x2(hv[g][0], hv[g][1]);
+            w[g][1] = pack_bf16x2(hv[g][2], hv[g][3]);
+          }
+          const bool ok = m < tile.rows;
+          store_h_pairs(static_cast<bf16_t*>(Cv), crow, n0 + wn * (WR / 4) + nb * 32, N, ok, half,
+                        partner, w);
+          if (Clo) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const uint32_t p0 = w[g][0], p1 = w[g][1];
+              w[g][0] = pack_bf16x2(hv[g][0] - __uint_as_float(p0 << 16),
+                                    hv[g][1] - __uint_as_float(p0 & 0xFFFF0000u));
+              w[g][1] = pack_bf16x2(hv[g][2] - __uint_as_float(p1 << 16),
+                                    hv[g][3] - __uint_as_float(p1 & 0xFFFF0000u));
             }
+            store_h_pairs(Clo, crow, n0 + wn * (WR / 4) + nb * 32, N, ok, half, partner, w);
           }
         }
       }
