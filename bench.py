@@ -240,10 +240,10 @@ def gate_up_kernel(w, rows):
     kmask = "true" if w.d % 64 else "false"
     if rows <= 32 * w.E:
         nb = 1 if rows <= 16 * w.E else 2
-        return f"expert_stream_kernel<true, 1, {nb}>", "expert_stream_kernel", "hbm"
+        return f"expert_stream_kernel<true, 1, {nb}, false>", "expert_stream_kernel", "hbm"
     if rows >= 2 * 384 * w.E:
         return f"expert_gemm_tall_kernel<true, {kmask}>", "expert_gemm_bf16_kernel", "mfma"
-    return f"expert_gemm_bf16_kernel<true, 8, {kmask}>", "expert_gemm_bf16_kernel", "mfma"
+    return f"expert_gemm_bf16_kernel<true, 8, {kmask}, false>", "expert_gemm_bf16_kernel", "mfma"
 
 
 def measure_layer(moe, w, dv, steps, warmup):
