@@ -209,11 +209,36 @@ moe_status launch_identity_rows(int T, int S, int32_t* sorted_token, int32_t* of
                                 hipStream_t s);
 moe_status launch_rms_norm(const void* x, const void* g, int T, int d, float eps, moe_dtype dt,
                            void* xn, hipStream_t s);
+// Few rows per expert: the weight-streaming kernels replace the tiled ones.
+inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
+
+// A decode-sized batch's permutation, derived inside the gate/up stream
+// kernel instead of by launch_permute: every workgroup ranks its own
+// expert's assignments in topk_idx (in assignment order, as launch_permute
+// does without a capacity), and the first workgroup of each expert writes
+// counts, offsets, sorted_token and inv_pos for the kernels after it. This
+// saves a launch and one dependent kernel boundary per layer call.
+constexpr int kSelfPermuteMax = 256;  // assignments: one per thread of a workgroup
+struct StreamPermute {
+  const int32_t* topk_idx;  // [n] expert ids in [0, E)
+  int n, k;
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E + 1]
+  int32_t* sorted_token;  // [n]
+  int32_t* inv_pos;       // [n]
+};
+inline bool stream_self_permute(int rows, int E, moe_dtype dt) {
+  return dt == MOE_BF16 && rows <= kSelfPermuteMax && use_stream_path(rows, E);
+}
+
 // h_lo: null, or (bf16 only) the second bf16 term of h, the rounding of
 // h - h_hi (see store_h); the down pass then multiplies both terms.
+// sp: null, or (when stream_self_permute holds) the routing from which the
+// stream kernel derives sorted_token and offsets, which it then writes.
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
-                          int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s);
+                          int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s,
+                          const StreamPermute* sp = nullptr);
 moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
                        int T, int d, int ffn, int E, int k, moe_dtype dt, void* y, int32_t* split,
                        hipStream_t s);
@@ -223,12 +248,10 @@ moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, 
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
                                  int d, int ffn, int E, int rows, void* h, bf16_t* h_lo,
-                                 int max_rows, hipStream_t s);
+                                 int max_rows, const StreamPermute* sp, hipStream_t s);
 moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* offsets,
                               const void* w_down, int d, int ffn, int E, int rows, void* y,
                               int32_t* split, int max_rows, int max_split, hipStream_t s);
-// Few rows per expert: the weight-streaming kernels replace the tiled ones.
-inline bool use_stream_path(int rows, int E) { return rows <= 32 * E; }
 // Router statistics (router_stats.hip): partial sums over router_stats_blocks(T)
 // blocks of `partial` floats per expert.
 int router_stats_blocks(int T);

@@ -965,8 +965,10 @@ void launch_256(const bf16_t* A, const bf16_t* Alo, const int32_t* sorted_token,
 
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
-                          int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s) {
+                          int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s,
+                          const StreamPermute* sp) {
   const int rows = T * k;
+  if (sp && !stream_self_permute(rows, E, dt)) return MOE_UNSUPPORTED;
   if (dt == MOE_F32) {
     expert_gemm_f32_kernel<true><<<dim3(rows, (ffn + 255) / 256), 256, 0, s>>>(
         static_cast<const float*>(x), sorted_token, offsets, E, static_cast<const float*>(w_gate),
@@ -979,8 +981,10 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
   const bf16_t* wu = static_cast<const bf16_t*>(w_up);
   if (use_stream_path(rows, E)) {
     const bool tiles = stream_needs_tiles(T);
+    // (with sp the stream kernel writes sorted_token and offsets, which
+    // the tile launch then reads)
     moe_status st = launch_gate_up_stream(x, sorted_token, offsets, w_gate, w_up, d, ffn, E, rows,
-                                          h, hl, tiles ? kStreamMaxRows : T, s);
+                                          h, hl, tiles ? kStreamMaxRows : T, sp, s);
     if (st != MOE_OK || !tiles) return st;
     launch_256<true, false>(xb, nullptr, sorted_token, offsets, E, wg, wu, ffn, d, h, hl, rows, 1,
                             0, nullptr, kStreamMaxRows, s);

@@ -52,14 +52,15 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
 }
 
 // One pass over reduction range [kbeg, kend) (kbeg a multiple of 64) for
-// token rows mb .. mb + 16*NB of expert rows starting at row0. TWO (down
+// token rows mb .. mb + 16*NB of expert rows starting at row0; gate/up
+// gathers row m's token tok[m]. TWO (down
 // only): h comes as two bf16 terms, A and Alo, and both are multiplied into
 // the same accumulators. GATE_UP with Clo non-null also writes the second
 // term of h.
 template <bool GATE_UP, int RB, int NB, bool TWO>
 __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
                                             const bf16_t* __restrict__ Alo,
-                                            const int32_t* __restrict__ sorted_token,
+                                            const int32_t* __restrict__ tok,
                                             const bf16_t* const (&wg)[RB],
                                             const bf16_t* const (&wu)[RB], int row0, int rows,
                                             int mb, int n0, int N, int K, int kbeg, int kend,
@@ -74,8 +75,7 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
   for (int t = 0; t < NB; ++t) {
     int m = mb + t * 16 + lr;
     m = m < rows ? m : mb;  // repeat a valid row past the end
-    const size_t arow = GATE_UP ? static_cast<size_t>(sorted_token[row0 + m])
-                                : static_cast<size_t>(row0 + m);
+    const size_t arow = GATE_UP ? static_cast<size_t>(tok[m]) : static_cast<size_t>(row0 + m);
     ap[t] = A + arow * K + lp * 8;
     apl[t] = TWO ? Alo + arow * K + lp * 8 : nullptr;
   }
@@ -194,24 +194,85 @@ __device__ __forceinline__ void stream_pass(const bf16_t* __restrict__ A,
   }
 }
 
+// Rows of expert e = blockIdx.y derived from the routing (StreamPermute):
+// one assignment per thread; two ballots per wave find the assignments to
+// experts below e (their count is e's first row) and those to e (ranked by
+// the assignments before them), whose tokens go to s_tok in row order.
+// Workgroup x = 0 of each expert also writes the permutation's outputs; an
+// id outside [0, E) (out of contract) gets inv_pos = -1, so the combine
+// skips it. Every thread of the workgroup takes part (two barriers).
+__device__ __forceinline__ void self_permute(const StreamPermute& sp, int e, int32_t* s_tok,
+                                             int* s_cnt, int& row0, int& rows) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, E = gridDim.y;
+  const int v = tid < sp.n ? sp.topk_idx[tid] : -1;
+  const uint64_t below = __ballot(v >= 0 && v < e), mine = __ballot(v == e);
+  if (lane == 0) {
+    s_cnt[wave] = __popcll(below);
+    s_cnt[SW + wave] = __popcll(mine);
+  }
+  __syncthreads();
+  int r0 = 0, n = 0, before = 0;
+#pragma unroll
+  for (int w = 0; w < SW; ++w) {
+    r0 += s_cnt[w];
+    n += s_cnt[SW + w];
+    before += w < wave ? s_cnt[SW + w] : 0;
+  }
+  const bool first = blockIdx.x == 0;
+  if (v == e) {
+    const int rank = before + __popcll(mine & ((1ull << lane) - 1));
+    const int t = tid / sp.k;
+    s_tok[rank] = t;
+    if (first) {
+      sp.sorted_token[r0 + rank] = t;
+      sp.inv_pos[tid] = r0 + rank;
+    }
+  }
+  if (first) {
+    if (e == 0 && tid < sp.n && (v < 0 || v >= E)) sp.inv_pos[tid] = -1;
+    if (tid == 0) {
+      sp.counts[e] = n;
+      sp.offsets[e] = r0;
+      if (e == E - 1) sp.offsets[E] = r0 + n;
+    }
+  }
+  __syncthreads();
+  row0 = r0;
+  rows = n;
+}
+
 // Grid: (ceil(N / (16 * RB * SW)), E, S). GATE_UP: A = x gathered by
 // sorted_token, weight rows from w_gate and w_up, C = h (bf16; with Clo
 // non-null its second term goes there). !GATE_UP: A = h rows (TWO: plus
 // their second terms Alo), weights w_down, C = y (24-bit format), part z at
-// element z * c_split.
-template <bool GATE_UP, int RB, int NB, bool TWO = false>
+// element z * c_split. SELF (gate/up): the rows come from the routing in sp
+// (self_permute) instead of sorted_token and offsets.
+template <bool GATE_UP, int RB, int NB, bool TWO = false, bool SELF = false>
 __global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ Alo,
     const int32_t* __restrict__ sorted_token, const int32_t* __restrict__ offsets,
     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N, int K,
     void* __restrict__ Cv, bf16_t* __restrict__ Clo, size_t c_split,
-    int32_t* __restrict__ split_out, int max_rows) {
+    int32_t* __restrict__ split_out, int max_rows, StreamPermute sp) {
   static_assert(!(TWO && GATE_UP), "two terms of h are an operand of the down pass only");
+  static_assert(GATE_UP || !SELF, "the down pass reads the gate/up pass's permutation");
+  static_assert(SW * 64 >= kSelfPermuteMax, "self_permute takes one assignment per thread");
   const int S = gridDim.z, z = blockIdx.z;
   if (!GATE_UP && split_out && blockIdx.x == 0 && blockIdx.y == 0 && z == 0 && threadIdx.x == 0)
     *split_out = S;
   const int e = blockIdx.y;
-  const int row0 = offsets[e], rows = offsets[e + 1] - row0;
+  int row0, rows;
+  const int32_t* tok = nullptr;  // gate/up: the token of each of the expert's rows
+  if constexpr (SELF) {
+    __shared__ int32_t s_tok[kSelfPermuteMax];
+    __shared__ int s_cnt[2 * SW];
+    self_permute(sp, e, s_tok, s_cnt, row0, rows);
+    tok = s_tok;
+  } else {
+    row0 = offsets[e];
+    rows = offsets[e + 1] - row0;
+    if (GATE_UP) tok = sorted_token + row0;
+  }
   if (rows == 0 || rows > max_rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * SW + wave) * 16 * RB;
@@ -232,8 +293,8 @@ __global__ __launch_bounds__(SW * 64) void expert_stream_kernel(
   }
   void* C = GATE_UP ? Cv : static_cast<void*>(static_cast<char*>(Cv) + z * c_split * 3);
   for (int mb = 0; mb < rows; mb += 16 * NB)
-    stream_pass<GATE_UP, RB, NB, TWO>(A, Alo, sorted_token, wg, wu, row0, rows, mb, n0, N, K,
-                                      kbeg, kend, C, Clo, lane);
+    stream_pass<GATE_UP, RB, NB, TWO>(A, Alo, tok, wg, wu, row0, rows, mb, n0, N, K, kbeg, kend,
+                                      C, Clo, lane);
 }
 
 // 16-row token blocks per pass: enough for the average expert of the batch.
@@ -248,17 +309,25 @@ constexpr int kRbGateUp = 1, kRbDown = 2;
 moe_status launch_gate_up_stream(const void* x, const int32_t* sorted_token,
                                  const int32_t* offsets, const void* w_gate, const void* w_up,
                                  int d, int ffn, int E, int rows, void* h, bf16_t* h_lo,
-                                 int max_rows, hipStream_t s) {
+                                 int max_rows, const StreamPermute* sp, hipStream_t s) {
   constexpr int RB = kRbGateUp;
   dim3 grid((ffn + 16 * RB * SW - 1) / (16 * RB * SW), E, 1);
+  if (sp && sp->n > kSelfPermuteMax) return MOE_UNSUPPORTED;
+  const StreamPermute none{};
   auto run = [&](auto kern) {
     kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(x), nullptr, sorted_token, offsets,
                                   static_cast<const bf16_t*>(w_gate),
                                   static_cast<const bf16_t*>(w_up), ffn, d, h, h_lo, size_t(0),
-                                  nullptr, max_rows);
+                                  nullptr, max_rows, sp ? *sp : none);
   };
-  if (token_blocks(rows, E) == 1) run(expert_stream_kernel<true, RB, 1>);
-  else run(expert_stream_kernel<true, RB, 2>);
+  const bool one = token_blocks(rows, E) == 1;
+  if (sp) {
+    if (one) run(expert_stream_kernel<true, RB, 1, false, true>);
+    else run(expert_stream_kernel<true, RB, 2, false, true>);
+  } else {
+    if (one) run(expert_stream_kernel<true, RB, 1>);
+    else run(expert_stream_kernel<true, RB, 2>);
+  }
   return launch_status();
 }
 
@@ -276,7 +345,7 @@ moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* 
   auto run = [&](auto kern) {
     kern<<<grid, SW * 64, 0, s>>>(static_cast<const bf16_t*>(h), h_lo, nullptr, offsets,
                                   static_cast<const bf16_t*>(w_down), nullptr, d, ffn, y, nullptr,
-                                  c_split, split, max_rows);
+                                  c_split, split, max_rows, StreamPermute{});
   };
   const bool one = token_blocks(rows, E) == 1;
   if (h_lo) {

@@ -195,19 +195,26 @@ moe_status moe_router_stats(const float* probs, const int32_t* counts, int T, in
 }
 
 // ev: NULL, or events [2..5] are recorded after the permutation, the gate/up
-// GEMM, the down GEMM and the combine.
+// GEMM, the down GEMM and the combine. A decode-sized bf16 batch has no
+// separate permutation: the gate/up stream kernel derives it from the
+// routing and writes the same outputs (stream_self_permute).
 static moe_status run_experts(const void* x, const int32_t* topk_idx, const float* topk_w,
                               const void* w_gate, const void* w_up, const void* w_down, int T,
                               int d, int ffn, int E, int k, moe_dtype dt, void* out,
                               moe_dtype out_dt, const Workspace& ws, int32_t* counts_out,
                               hipStream_t stream, hipEvent_t* ev) {
-  moe_status st = launch_permute(topk_idx, T, E, k, T, counts_out ? counts_out : ws.counts,
-                                 nullptr, ws.offsets, ws.sorted_token, ws.inv_pos,
-                                 ws.block_counts, stream);
-  if (st != MOE_OK) return st;
+  int32_t* counts = counts_out ? counts_out : ws.counts;
+  const bool self = stream_self_permute(T * k, E, dt);
+  moe_status st = MOE_OK;
+  if (!self) {
+    st = launch_permute(topk_idx, T, E, k, T, counts, nullptr, ws.offsets, ws.sorted_token,
+                        ws.inv_pos, ws.block_counts, stream);
+    if (st != MOE_OK) return st;
+  }
   if (ev) hipEventRecord(ev[2], stream);
+  const StreamPermute sp{topk_idx, T * k, k, counts, ws.offsets, ws.sorted_token, ws.inv_pos};
   st = launch_gate_up(x, ws.sorted_token, ws.offsets, w_gate, w_up, T, d, ffn, E, k, dt, ws.h,
-                      ws.h_lo, stream);
+                      ws.h_lo, stream, self ? &sp : nullptr);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], stream);
   st = launch_down(ws.h, ws.h_lo, ws.offsets, w_down, T, d, ffn, E, k, dt, ws.y, ws.split,

@@ -188,8 +188,7 @@ ROW_SPLITS = [
     ([384, 385, 1151, 1153], 64, 96),        # tall tiles: exactly one tile, one row more, 3 and 4 tiles
     ([257, 511, 512, 513, 31, 33], 64, 96),  # 256 x 256 tiles
     ([1, 32, 33, 800], 64, 96),              # tiny experts beside a large one
-    # tall tiles with light experts: tiles of at most 128 rows load only
-    # their first 128 token rows per step (the 129-row tile loads all 384)
+    # tall tiles with light experts beside a heavy one (tiles of 1 to 129 rows)
     ([5000, 100, 20, 1, 128, 129], 64, 128),
     ([4000, 1, 65, 128, 129], 1040, 1024),   # one-term h, reduction tails
 ]
@@ -309,6 +308,45 @@ def test_forward_parity_shapes(M, T, d, ffn, E, k, bias):
     torch.cuda.synchronize()
     compare_layer(host(out), inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
                   k, inp["router_bias"], layer_tol(d, ffn, "bf16"))
+
+
+# Decode-sized bf16 batches (at most 256 assignments on the weight-streaming
+# path): the gate/up stream kernel ranks each expert's assignments itself and
+# writes the permutation that the down pass and the combine read; the counts
+# come from the same place. Around it: 264 assignments (separate permutation
+# kernel), E at its limit, and experts above 64 rows, whose tile launch reads
+# the permutation the stream kernel wrote.
+DECODE_SIZED = [
+    # T, d, ffn, E, k, router bias (None, or (expert, bias) pairs)
+    (32, 128, 192, 8, 2, None),
+    (128, 64, 96, 8, 2, None),          # 256 assignments, the limit
+    (132, 64, 96, 16, 2, None),         # 264: streamed, permutation kernel
+    (40, 64, 96, 64, 6, None),
+    (16, 64, 96, 256, 16, None),        # E = 256, 256 assignments
+    (128, 64, 96, 8, 2, ((3, 60.0), (5, 30.0))),  # every token on experts 3 and 5: both tiled
+    (100, 1024, 1024, 4, 1, ((2, 60.0),)),        # one-term h, all 100 rows on expert 2
+]
+
+
+@pytest.mark.parametrize("T,d,ffn,E,k,bias", DECODE_SIZED)
+def test_forward_decode_sized(M, T, d, ffn, E, k, bias):
+    say(f"moe_forward decode-sized T={T} d={d} ffn={ffn} E={E} k={k} bias={bias}")
+    inp = wl.make_custom_inputs(T, d, ffn, E, "bf16", seed=11)
+    if bias is not None:
+        b = np.zeros(E, dtype=np.float32)
+        for e, v in bias:
+            b[e] = v
+        inp["router_bias"] = b
+    dv = {n: dev_tensor(v) for n, v in inp.items()}
+    out, ex = M.moe_forward(dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], k,
+                            router_bias=dv["router_bias"], want_counts=True)
+    torch.cuda.synchronize()
+    st = compare_layer(host(out), inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"],
+                       inp["w_down"], k, inp["router_bias"], layer_tol(d, ffn, "bf16"))
+    diff = np.abs(host(ex["counts"]).astype(np.int64) - O.expert_counts(st["ref_idx"], E))
+    assert diff.sum() <= 2 * st["near_ties"]
+    if bias is not None and st["near_ties"] == 0:
+        assert all(host(ex["counts"])[e] == T for e, _ in bias)
 
 
 def test_forward_zero_tokens(M):
