@@ -89,8 +89,9 @@ const char* moe_status_string(moe_status s);
  * shape: routing results, per-expert offsets, the permutation, the hidden
  * activations h [T*k, ffn] (in dt; twice that for a bf16 layer narrower than
  * 1024 in d or ffn, whose h takes two bf16 terms) and expert outputs
- * y [T*k, d] (up to four partial sums; 3 bytes per element for bf16 layers,
- * 4 for fp32). Returns 0 for invalid or unsupported shapes. Host-only; no
+ * y [T*k, d] (as many partial sums as the down pass may cut its reduction
+ * into: one per 12 steps of 64 along ffn, between one and four; 3 bytes per
+ * element for bf16 layers, 4 for fp32). Returns 0 for invalid or unsupported shapes. Host-only; no
  * device access. */
 size_t moe_workspace_size(int T, int d, int ffn, int E, int k, moe_dtype dt);
 

@@ -12,6 +12,18 @@ constexpr int kWave = 64;         // CDNA wavefront width
 constexpr int kMaxExperts = 256;  // library limit on E
 constexpr int kMaxTopK = 16;      // library limit on k
 constexpr int kMaxDownSplit = 4;  // most parts the down GEMM's reduction is cut into
+constexpr int kMinSplitSteps = 12;    // tiled down pass: fewest 64-wide steps per part
+constexpr int kMinStreamChunks = 16;  // streaming down pass: fewest 64-wide chunks per part
+
+// Most parts the down pass can cut a reduction of length ffn into, on either
+// path (the device picks the count from the real tile count, never more):
+// the workspace holds that many partial sums of y.
+inline int down_split_bound(int ffn) {
+  const int tiled = ((ffn + 63) / 64) / kMinSplitSteps;
+  const int stream = (ffn / 64) / kMinStreamChunks;
+  const int s = tiled > stream ? tiled : stream;
+  return s < 1 ? 1 : (s > kMaxDownSplit ? kMaxDownSplit : s);
+}
 constexpr int kPermMaxBlocks = 256;            // most workgroups of the permutation
 constexpr long long kPermBlockedFrom = 4096;   // up to this many assignments: one workgroup
 constexpr long long kMaxAssignments = (1ll << 31) - (1ll << 20);  // T*k must stay below
@@ -121,7 +133,7 @@ struct Workspace {
   int32_t* inv_pos;       // [T*k]
   void* h;                // [T*k, ffn] in dt
   void* h_lo;             // [T*k, ffn] bf16: second term of h (two_term_h), else null
-  void* y;                // [kMaxDownSplit, T*k, d] partial sums of the down GEMM (y_bytes(dt) each)
+  void* y;                // [down_split_bound(ffn), T*k, d] partial sums of the down GEMM (y_bytes(dt) each)
   int32_t* split;         // [1] number of partial sums in y
   int32_t* block_counts;  // [kPermMaxBlocks * E] per-block expert histograms of the permutation
   size_t bytes;
@@ -144,7 +156,7 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   w.inv_pos = reinterpret_cast<int32_t*>(take(tk * 4));
   w.h = take(tk * static_cast<size_t>(ffn) * es);
   w.h_lo = two_term_h(d, ffn, dt) ? take(tk * static_cast<size_t>(ffn) * es) : nullptr;
-  w.y = take(kMaxDownSplit * tk * static_cast<size_t>(d) * y_bytes(dt));
+  w.y = take(down_split_bound(ffn) * tk * static_cast<size_t>(d) * y_bytes(dt));
   w.split = reinterpret_cast<int32_t*>(take(4));
   w.block_counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(kPermMaxBlocks) * E * 4));
   w.bytes = off;
@@ -159,7 +171,7 @@ struct ExtWorkspace {
   int32_t* off_s;         // [n_shared+1]
   void* h_s;              // [n_shared*T, shared_ffn] in dt
   void* h_s_lo;           // second term of h_s (two_term_h for shared_ffn), else null
-  void* y_s;              // [kMaxDownSplit, n_shared*T, d] (y_bytes(dt) each)
+  void* y_s;              // [down_split_bound(shared_ffn), n_shared*T, d] (y_bytes(dt) each)
   int32_t* split_s;       // [1]
   size_t bytes;
 };
@@ -180,7 +192,7 @@ inline ExtWorkspace carve_ext_workspace(void* base, int T, int d, int ffn, int E
     w.h_s = take(ts * static_cast<size_t>(shared_ffn) * es);
     w.h_s_lo = two_term_h(d, shared_ffn, dt) ? take(ts * static_cast<size_t>(shared_ffn) * es)
                                              : nullptr;
-    w.y_s = take(kMaxDownSplit * ts * static_cast<size_t>(d) * y_bytes(dt));
+    w.y_s = take(down_split_bound(shared_ffn) * ts * static_cast<size_t>(d) * y_bytes(dt));
     w.split_s = reinterpret_cast<int32_t*>(take(4));
   }
   w.bytes = off;

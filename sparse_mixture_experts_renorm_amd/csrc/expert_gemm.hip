@@ -61,7 +61,6 @@ namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int kMinSplitSteps = 12;
 
 struct Tile {
   int e, row0, rows, nt;
@@ -1016,12 +1015,13 @@ moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, 
   const bf16_t* hl = static_cast<const bf16_t*>(h_lo);
   const bf16_t* wd = static_cast<const bf16_t*>(w_down);
   const size_t c_split = static_cast<size_t>(rows) * d;
+  const int max_split = down_split_bound(ffn);  // the parts the workspace holds
   if (use_stream_path(rows, E)) {
     // with a tile launch as well, both write one partial sum (the combine
     // reads one count of parts for every row)
     const bool tiles = stream_needs_tiles(T);
     moe_status st = launch_down_stream(h, hl, offsets, w_down, d, ffn, E, rows, y, split,
-                                       tiles ? kStreamMaxRows : T, tiles ? 1 : kMaxDownSplit, s);
+                                       tiles ? kStreamMaxRows : T, tiles ? 1 : max_split, s);
     if (st != MOE_OK || !tiles) return st;
     if (hl)
       launch_256<false, true>(hb, hl, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, rows,
@@ -1034,19 +1034,19 @@ moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, 
   if (hl) {
     // two terms of h: 128 output rows per 256 x 256 tile
     launch_256<false, true>(hb, hl, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, rows,
-                            kMaxDownSplit, c_split, split, 0, s);
+                            max_split, c_split, split, 0, s);
     return launch_status();
   }
   if (use_tall_tiles(rows, E)) {
     auto kern = ffn % TK ? expert_gemm_tall_kernel<false, true> : expert_gemm_tall_kernel<false, false>;
     const int ncu = cu_count();
-    kern<<<tall_grid(rows, E, (d + TW - 1) / TW, kMaxDownSplit, ncu), NW3 * 64, 0, s>>>(
-        hb, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, kMaxDownSplit, ncu, c_split,
+    kern<<<tall_grid(rows, E, (d + TW - 1) / TW, max_split, ncu), NW3 * 64, 0, s>>>(
+        hb, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, max_split, ncu, c_split,
         split, 0);
     return launch_status();
   }
   launch_256<false, false>(hb, nullptr, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, rows,
-                           kMaxDownSplit, c_split, split, 0, s);
+                           max_split, c_split, split, 0, s);
   return launch_status();
 }
 

@@ -339,7 +339,8 @@ moe_status launch_down_stream(const void* h, const bf16_t* h_lo, const int32_t* 
   // until the grid holds about two waves per SIMD
   const int nx = (d + 16 * RB * SW - 1) / (16 * RB * SW);
   int S = 1;
-  while (2 * S <= max_split && nx * E * S * SW < 2048 && ffn / 64 >= 2 * S * 16) S *= 2;
+  while (2 * S <= max_split && nx * E * S * SW < 2048 && ffn / 64 >= 2 * S * kMinStreamChunks)
+    S *= 2;
   dim3 grid(nx, E, S);
   const size_t c_split = static_cast<size_t>(rows) * d;
   auto run = [&](auto kern) {

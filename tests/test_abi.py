@@ -35,6 +35,19 @@ def test_status_strings(L):
     assert m.status_string(99) == "MOE_UNKNOWN_STATUS"
 
 
+def test_workspace_holds_reachable_splits(L):
+    """The down pass cuts its reduction over ffn into at most one part per
+    12 steps of 64 (one to four parts), and the workspace holds exactly that
+    many partial sums of y (3 bytes per element in a bf16 layer), besides h
+    (two bf16 terms below width 1024) and a few small arrays."""
+    T, d, E, k = 8192, 2048, 64, 8
+    for ffn, parts in [(1408, 1), (2816, 3), (14336, 4), (512, 1), (768, 1), (1536, 2)]:
+        n = L.moe_workspace_size(T, d, ffn, E, k, BF16)
+        y = T * k * d * 3
+        h = T * k * ffn * 2 * (2 if ffn < 1024 else 1)
+        assert parts * y + h <= n < parts * y + h + (8 << 20), (ffn, n)
+
+
 def test_workspace_size(L):
     T, d, ffn, E, k = 4096, 4096, 14336, 8, 2
     n = m.moe_workspace_size(T, d, ffn, E, k, BF16)
