@@ -68,27 +68,59 @@ struct Tile {
   int half;   // -1: the whole column tile; 0 or 1: that half of its weight rows
 };
 
-// Row tiles of BM rows per expert, as a prefix: pref[e] = sum over e' < e of
-// ceil(M_e' / BM), for e = 0 .. E (M_e = offsets[e+1] - offsets[e]); experts
-// with at most min_rows rows get no tiles (the weight-streaming kernel takes
-// them). Serial form, for the host; the kernels build the same array with
-// one wave (map_tile).
+// Row tiles of BM rows per expert, ceil(M_e / BM) (M_e = offsets[e+1] -
+// offsets[e]); experts with at most min_rows rows get none (the
+// weight-streaming kernel takes them).
 __host__ __device__ inline int expert_row_tiles(int m, int BM, int min_rows) {
   return m > min_rows ? (m + BM - 1) / BM : 0;
 }
+// An expert whose rows fill at most a third of a tile is light: its one
+// tile takes about 60% of a full tile's time (the loads of a whole tile,
+// one token block of MFMAs per wave), so the tile list keeps the light
+// experts' tiles apart and every XCD gets its share of both kinds.
+__host__ __device__ inline bool light_expert(int m, int BM) { return 3 * m <= BM; }
+// The row-tile prefixes, heavy experts in pref[0 .. E] and light ones in
+// pref[E+1 .. 2E+1]: pref[e] = sum over heavy e' < e of their row tiles, and
+// likewise for the light ones. Serial form, for the host; the kernels build
+// the same arrays with one wave (map_tile).
 template <int BM>
 __host__ __device__ inline void row_tile_prefix(const int32_t* __restrict__ offsets, int E,
                                                 int* pref, int min_rows = 0) {
-  pref[0] = 0;
-  for (int e = 0; e < E; ++e)
-    pref[e + 1] = pref[e] + expert_row_tiles(offsets[e + 1] - offsets[e], BM, min_rows);
+  int* pl = pref + E + 1;
+  pref[0] = pl[0] = 0;
+  for (int e = 0; e < E; ++e) {
+    const int m = offsets[e + 1] - offsets[e], t = expert_row_tiles(m, BM, min_rows);
+    const bool light = light_expert(m, BM);
+    pref[e + 1] = pref[e] + (light ? 0 : t);
+    pl[e + 1] = pl[e] + (light ? t : 0);
+  }
+}
+
+// The split count for `base` tiles per part (see assign_tile): fewest rounds
+// per part, counted in whole tiles, with at least kMinSplitSteps of the nk
+// reduction steps in each part.
+__host__ __device__ inline int choose_split(int base, int max_split, int n_cu, int nk) {
+  int S = 1, best_rounds = (base + n_cu - 1) / n_cu;  // rounds of S-tiles
+  for (int c = 2; c <= max_split && c * kMinSplitSteps <= nk; ++c) {
+    const int rounds = (base * c + n_cu - 1) / n_cu;
+    if (rounds * S < best_rounds * c) {  // rounds/c < best_rounds/S
+      S = c;
+      best_rounds = rounds;
+    }
+  }
+  return S;
 }
 
 // Tile of workgroup `block` among tiles of BM rows, given the experts' row
-// offsets and their row-tile prefix pref [E+1]: res = {expert (-1: none),
+// offsets and their row-tile prefixes pref [2E+2]: res = {expert (-1: none),
 // first permuted row, rows, column tile, split part, split count S, half
 // (-1: whole column tile; 0 or 1: that half of its weight rows)}.
-// The tile list runs over the experts in order; inside an expert over the
+// There are two tile lists, of the heavy experts and of the light ones;
+// each is cut into 8 contiguous ranges of equal count, and XCD x runs its
+// range of both, the light tiles spread evenly among the heavy ones (so the
+// light experts' weight reads overlap other tiles' MFMA work and no XCD
+// gets the light tiles of all of them). A list runs over its experts in
+// order; inside an expert over the
 // split parts, and inside a part over column tiles and, for each, over its
 // row tiles -- or, when the expert has more rows than the operation has
 // weight rows (wrows), over row tiles and, for each, over its column tiles.
@@ -96,9 +128,7 @@ __host__ __device__ inline void row_tile_prefix(const int32_t* __restrict__ offs
 // through its L2, and the smaller one is what is read again per round.
 // With max_split > 1 the reduction dimension may be cut into S <= max_split
 // parts, each a separate tile whose partial result goes to its own output
-// slice; S is chosen from the real tile count to minimise the number of
-// rounds on n_cu CUs, counted in units of a whole tile, with at least
-// kMinSplitSteps of the nk reduction steps in every part (shorter parts
+// slice; S is chosen from the real tile count (choose_split; shorter parts
 // would spend more on the extra partial sums than they save).
 // With TAIL, an XCD whose tile count leaves a last round at most half full
 // (r tiles for its n_cu/8 CUs, 2r <= n_cu/8) runs those r tiles as 2r
@@ -111,48 +141,53 @@ template <int BM, bool TAIL>
 __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets, const int* pref,
                                             int E, int nN, int max_split, int n_cu, int nk,
                                             int wrows, int block, int* res) {
-  const int base = pref[E] * nN;
-  int S = 1, best_rounds = (base + n_cu - 1) / n_cu;  // rounds of S-tiles
-  for (int c = 2; c <= max_split && c * kMinSplitSteps <= nk; ++c) {
-    const int rounds = (base * c + n_cu - 1) / n_cu;
-    if (rounds * S < best_rounds * c) {  // rounds/c < best_rounds/S
-      S = c;
-      best_rounds = rounds;
-    }
-  }
-  const int total = base * S;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int* pl = pref + E + 1;
+  const int base_h = pref[E] * nN, base_l = pl[E] * nN;  // tiles of one split part
+  const int S = choose_split(base_h + base_l, max_split, n_cu, nk);
+  const int per_h = (base_h * S + kXcds - 1) / kXcds, per_l = (base_l * S + kXcds - 1) / kXcds;
   const int xcd = block % kXcds, slot = block / kXcds;
-  const int first = xcd * per_xcd;
-  int cnt = total - first;  // tiles of this XCD
-  cnt = cnt < 0 ? 0 : (cnt > per_xcd ? per_xcd : cnt);
-  int L = -1, half = -1;
+  auto share = [&](int base, int per) {  // tiles of one list on this XCD
+    const int c = base * S - xcd * per;
+    return c < 0 ? 0 : (c > per ? per : c);
+  };
+  const int cnt_h = share(base_h, per_h), cnt_l = share(base_l, per_l), cnt = cnt_h + cnt_l;
+  int li = -1, half = -1;  // position in this XCD's order
   if (TAIL) {
     const int cpx = n_cu / kXcds > 1 ? n_cu / kXcds : 1, r = cnt % cpx;
     const int nfull = (r > 0 && 2 * r <= cpx) ? cnt - r : cnt;
     if (slot < nfull) {
-      L = first + slot;
+      li = slot;
     } else if (slot < nfull + 2 * (cnt - nfull)) {
-      L = first + nfull + (slot - nfull) / 2;
+      li = nfull + (slot - nfull) / 2;
       half = (slot - nfull) & 1;
     }
   } else if (slot < cnt) {
-    L = first + slot;
+    li = slot;
   }
   res[0] = -1;
   res[5] = S;
   res[6] = half;
-  if (L < 0) return;
-  // the expert of tile L: the first e with pref[e+1] * nN * S > L
+  if (li < 0) return;
+  // position li holds a light tile where floor(i * cnt_l / cnt) steps up
+  // (no division when the XCD has no light tiles: the 64-bit one is slow)
+  int nl0 = 0;
+  bool light = false;
+  if (cnt_l > 0) {
+    nl0 = static_cast<int>(static_cast<long long>(li) * cnt_l / cnt);
+    light = static_cast<int>(static_cast<long long>(li + 1) * cnt_l / cnt) > nl0;
+  }
+  const int* pc = light ? pl : pref;
+  int L = light ? xcd * per_l + nl0 : xcd * per_h + (li - nl0);
+  // the expert of tile L of its list: the first e with pc[e+1] * nN * S > L
   const int per_row_tile = nN * S;
   int lo = 0, hi = E - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (pref[mid + 1] * per_row_tile > L) hi = mid; else lo = mid + 1;
+    if (pc[mid + 1] * per_row_tile > L) hi = mid; else lo = mid + 1;
   }
   const int e = lo;
-  L -= pref[e] * per_row_tile;
-  const int mt = pref[e + 1] - pref[e], m = offsets[e + 1] - offsets[e];
+  L -= pc[e] * per_row_tile;
+  const int mt = pc[e + 1] - pc[e], m = offsets[e + 1] - offsets[e];
   const int te = mt * nN;  // tiles of one split part of expert e
   const int ks = L / te;
   L -= ks * te;
@@ -171,8 +206,8 @@ __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets,
   res[4] = ks;
 }
 
-// LDS the tile map needs: the seven results, then the prefix.
-constexpr int kMapLdsInts = 8 + kMaxExperts + 1;
+// LDS the tile map needs: the seven results, then the two prefixes.
+constexpr int kMapLdsInts = 8 + 2 * (kMaxExperts + 1);
 static_assert(kMaxExperts <= 4 * kWave, "map_tile sums four experts per lane");
 
 // Map this workgroup to its tile; returns false if it has none. Wave 0
@@ -183,29 +218,49 @@ template <int BM, bool TAIL = false>
 __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int nN, int max_split,
                          int n_cu, int nk, int min_rows, int wrows, Tile* out, int* s_map) {
   int* pref = s_map + 8;
+  int* pl = pref + E + 1;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int c[4], sum = 0;
+    int ch[4], cl[4], sh = 0, sl = 0;  // row tiles of heavy / light experts
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
-      c[q] = e < E ? expert_row_tiles(offsets[e + 1] - offsets[e], BM, min_rows) : 0;
-      sum += c[q];
+      const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
+      const int t = expert_row_tiles(m, BM, min_rows);
+      const bool light = light_expert(m, BM);
+      ch[q] = light ? 0 : t;
+      cl[q] = light ? t : 0;
+      sh += ch[q];
+      sl += cl[q];
     }
-    int incl = sum;
+    int ih = sh, il = sl;
 #pragma unroll
     for (int dl = 1; dl < kWave; dl <<= 1) {
-      const int v = __shfl_up(incl, dl, kWave);
-      if (lane >= dl) incl += v;
+      const int v = __shfl_up(ih, dl, kWave);
+      if (lane >= dl) ih += v;
     }
-    int run = incl - sum;
+    if (__any(sl > 0)) {  // the light list's scan only when it has tiles
+#pragma unroll
+      for (int dl = 1; dl < kWave; dl <<= 1) {
+        const int v = __shfl_up(il, dl, kWave);
+        if (lane >= dl) il += v;
+      }
+    }
+    int rh = ih - sh, rl = il - sl;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
-      if (e < E) pref[e] = run;
-      run += c[q];
+      if (e < E) {
+        pref[e] = rh;
+        pl[e] = rl;
+      }
+      rh += ch[q];
+      rl += cl[q];
     }
-    if (lane == kWave - 1) pref[E] = incl;
+    if (lane == kWave - 1) {
+      pref[E] = ih;
+      pl[E] = il;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0)
@@ -920,7 +975,8 @@ constexpr int kWaves = MOE_GEMM_WAVES;
 unsigned tile_grid(int rows, int E, int BM, int nN, int splits) {
   const long long max_mt = rows / BM + (rows < E ? rows : E);
   const long long g = max_mt * nN * splits;
-  return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds);
+  // (+1 slot per XCD: the heavy and light lists' shares each round up)
+  return static_cast<unsigned>((g + kXcds - 1) / kXcds * kXcds + kXcds);
 }
 
 // tile_grid plus the half-width tail tiles' extra slots (assign_tile's TAIL)

@@ -28,8 +28,10 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
   // (e, column tile, part, first row) -> rows
   std::map<std::tuple<int, int, int, int>, int> rows_of;
   int S = -1;
-  std::vector<int> pref(E + 1);
+  std::vector<int> pref(2 * E + 2);
   row_tile_prefix<BM>(off.data(), E, pref.data(), min_rows);
+  // light experts' tiles per XCD (the halves of a split tile count once)
+  std::map<std::tuple<int, int, int, int>, int> light_xcd;
   for (unsigned b = 0; b < grid; ++b) {
     int res[7];
     assign_tile<BM, TAIL>(off.data(), pref.data(), E, nN, max_split, n_cu, nk, wrows,
@@ -47,6 +49,7 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
                     res[3], res[4], res[6]), 1;
     // key by the first row; the rows must cut the expert into its row tiles
     seen[{e, res[1], res[3], res[4]}][res[6] + 1] += 1;
+    if (light_expert(off[e + 1] - off[e], BM)) light_xcd[{e, res[1], res[3], res[4]}] = b % kXcds;
     const auto key = std::make_tuple(e, res[3], res[4], res[1]);
     const auto it = rows_of.find(key);
     if (it != rows_of.end() && it->second != res[2])
@@ -91,6 +94,15 @@ static int check(const std::vector<int32_t>& off, int E, int rows_bound, int nN,
     const bool halves = c[0] == 0 && c[1] == 1 && c[2] == 1;
     if (!whole && !halves)
       return printf("tile assigned %d whole, %d + %d halves\n", c[0], c[1], c[2]), 1;
+  }
+  // every XCD runs at most its even share of the light experts' tiles
+  {
+    std::vector<int> per(kXcds, 0);
+    for (const auto& kv : light_xcd) per[kv.second] += 1;
+    const int share = (static_cast<int>(light_xcd.size()) + kXcds - 1) / kXcds;
+    for (int x = 0; x < kXcds; ++x)
+      if (per[x] > share)
+        return printf("XCD %d runs %d light tiles, more than its share %d\n", x, per[x], share), 1;
   }
   *tiles_seen += expected;
   return 0;
