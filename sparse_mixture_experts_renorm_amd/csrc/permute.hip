@@ -293,13 +293,31 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
   __shared__ int base[kMaxExperts];
   __shared__ int start[kMaxExperts];
   __shared__ int wave_cnt[kPermWaves][kMaxExperts];
+  __shared__ int part_tot[kPermThreads], part_pre[kPermThreads];
   const int tid = threadIdx.x, b = blockIdx.x, nb = gridDim.x;
-  for (int e = tid; e < E; e += kPermThreads) {
+  // Column sums of the count table (every block's total and the blocks
+  // before b): G groups of E threads, group g summing blocks g, g + G, ...
+  // (independent loads, one memory round trip for up to G blocks), then E
+  // threads add the G partial sums (integers: exact in any order). G is at
+  // most the number of blocks, so no group sums nothing.
+  const int G = min(kPermThreads / E, nb);
+  if (tid < G * E) {
+    const int g = tid / E, e = tid - g * E;
     int tot = 0, pre = 0;
-    for (int bb = 0; bb < nb; ++bb) {
+    for (int bb = g; bb < nb; bb += G) {
       const int c = block_counts[static_cast<size_t>(bb) * E + e];
       pre += bb < b ? c : 0;
       tot += c;
+    }
+    part_tot[tid] = tot;
+    part_pre[tid] = pre;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermThreads) {
+    int tot = 0, pre = 0;
+    for (int g = 0; g < G; ++g) {
+      tot += part_tot[g * E + e];
+      pre += part_pre[g * E + e];
     }
     cnt[e] = tot;
     base[e] = pre;
