@@ -240,7 +240,11 @@ def gate_up_kernel(w, rows):
     kmask = "true" if w.d % 64 else "false"
     if rows <= 32 * w.E:
         nb = 1 if rows <= 16 * w.E else 2
-        return f"expert_stream_kernel<true, 1, {nb}, false>", "expert_stream_kernel", "hbm"
+        # bf16 batches of at most 256 assignments derive their permutation
+        # inside this kernel (its last template argument)
+        self_perm = "true" if w.dtype == "bf16" and rows <= 256 else "false"
+        return (f"expert_stream_kernel<true, 1, {nb}, false, {self_perm}>", "expert_stream_kernel",
+                "hbm")
     if rows >= 2 * 384 * w.E:
         return f"expert_gemm_tall_kernel<true, {kmask}>", "expert_gemm_bf16_kernel", "mfma"
     return f"expert_gemm_bf16_kernel<true, 8, {kmask}, false>", "expert_gemm_bf16_kernel", "mfma"

@@ -117,10 +117,11 @@ __host__ __device__ inline int choose_split(int base, int max_split, int n_cu, i
 // (-1: whole column tile; 0 or 1: that half of its weight rows)}.
 // There are two tile lists, of the heavy experts and of the light ones;
 // each is cut into 8 contiguous ranges of equal count, and XCD x runs its
-// range of both, the light tiles spread evenly among the heavy ones (so the
-// light experts' weight reads overlap other tiles' MFMA work and no XCD
-// gets the light tiles of all of them). A list runs over its experts in
-// order; inside an expert over the
+// range of the heavy list, then its range of the light one (so no XCD gets
+// the light tiles of all of them while the others run only heavy tiles,
+// and the heavy tiles' rounds keep their shared operands in L2; light
+// tiles spread among the heavy ones were no faster and fetched 30% more).
+// A list runs over its experts in order; inside an expert over the
 // split parts, and inside a part over column tiles and, for each, over its
 // row tiles -- or, when the expert has more rows than the operation has
 // weight rows (wrows), over row tiles and, for each, over its column tiles.
@@ -170,14 +171,9 @@ __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets,
   if (li < 0) return;
   // position li holds a light tile where floor(i * cnt_l / cnt) steps up
   // (no division when the XCD has no light tiles: the 64-bit one is slow)
-  int nl0 = 0;
-  bool light = false;
-  if (cnt_l > 0) {
-    nl0 = static_cast<int>(static_cast<long long>(li) * cnt_l / cnt);
-    light = static_cast<int>(static_cast<long long>(li + 1) * cnt_l / cnt) > nl0;
-  }
+  const bool light = li >= cnt_h;
   const int* pc = light ? pl : pref;
-  int L = light ? xcd * per_l + nl0 : xcd * per_h + (li - nl0);
+  int L = light ? xcd * per_l + (li - cnt_h) : xcd * per_h + li;
   // the expert of tile L of its list: the first e with pc[e+1] * nN * S > L
   const int per_row_tile = nN * S;
   int lo = 0, hi = E - 1;
