@@ -171,8 +171,10 @@ moe_status moe_forward(const void* x, const void* w_router, const void* w_gate,
 /* moe_forward that also records caller-created events on `stream` between
  * its stages, for per-kernel timing: stage_events[0] before the router,
  * [1] after the router, [2] after the permutation, [3] after the gate/up
- * GEMM, [4] after the down GEMM, [5] after the combine (6 events, none NULL).
- * Results are identical to moe_forward's. */
+ * GEMM, [4] after the down GEMM, [5] after the combine (6 events, none NULL;
+ * a bf16 batch of at most 256 assignments on the weight-streaming kernels
+ * has no separate permutation, its gate/up kernel derives it, so [1] and
+ * [2] are recorded back to back). Results are identical to moe_forward's. */
 moe_status moe_forward_profiled(const void* x, const void* w_router, const void* w_gate,
                                 const void* w_up, const void* w_down, const float* router_bias,
                                 int T, int d, int ffn, int E, int k, moe_dtype dt,

@@ -37,8 +37,10 @@
 // rows to those lanes, and the row's half of the 256-byte bank line (r & 1)
 // together with its slot gives 16 distinct bank groups.
 // The MFMA takes the weight fragment as its first operand, so each lane's
-// accumulators hold 4 consecutive output columns of one row, which the
-// epilogue writes as one 8-byte (h) or 16-byte (y) store.
+// accumulators hold 4 consecutive output columns of one row. The epilogues
+// turn that layout into whole rows per store instruction: through a per-wave
+// LDS tile (y of both tile shapes, h of the 256 x 256 tiles) or, for h of
+// the tall tiles, by an exchange between lane pairs.
 //
 // Tile schedule: the host sizes the grid from an upper bound on the tile
 // count; each workgroup reads the per-expert offsets, counts the real tiles
@@ -48,7 +50,8 @@
 // weight tile take the same time. Workgroups are handed
 // to the 8 XCDs round-robin, so consecutive tiles of the schedule are given
 // to workgroups on the same XCD (sharing its L2): each XCD takes a
-// contiguous eighth of the tile list. Inside an expert (and split part) the
+// contiguous eighth of the tile list (of each of the two lists, heavy and
+// light experts: see assign_tile). Inside an expert (and split part) the
 // list runs over column tiles and, for each, over its row tiles, so the row
 // tiles that share a weight tile run side by side and the weights go
 // through L2 about once (with the row tiles of one column tile spread over
@@ -169,8 +172,7 @@ __host__ __device__ inline void assign_tile(const int32_t* __restrict__ offsets,
   res[5] = S;
   res[6] = half;
   if (li < 0) return;
-  // position li holds a light tile where floor(i * cnt_l / cnt) steps up
-  // (no division when the XCD has no light tiles: the 64-bit one is slow)
+  // the XCD's heavy tiles first, then its light ones
   const bool light = li >= cnt_h;
   const int* pc = light ? pl : pref;
   int L = light ? xcd * per_l + (li - cnt_h) : xcd * per_h + li;

@@ -23,7 +23,10 @@
 //     order;
 //   - experts without rows exit at once, so their weights are never read;
 //     so do experts with more than max_rows rows, which a tiled launch takes
-//     (their weights would otherwise be read once per 16*NB rows).
+//     (their weights would otherwise be read once per 16*NB rows);
+//   - for a bf16 batch of at most 256 assignments the gate/up kernel ranks
+//     each expert's assignments itself (self_permute) instead of reading a
+//     permutation, and writes that permutation for the kernels after it.
 // Token rows past an expert's count repeat a valid row; their results are
 // never stored.
 #include "common.h"
