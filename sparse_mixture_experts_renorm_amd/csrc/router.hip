@@ -7,7 +7,10 @@
 // exact: softmax is strictly increasing, and the stable sort's tie rule
 // becomes "lower expert index first", with +0.0 and -0.0 equal.
 //
-// Layout on gfx950: one wavefront routes one token. Lane l owns experts
+// The logits come from route_bf16_kernel (16 tokens per workgroup on the
+// bf16 MFMA), from route_bf16_narrow_kernel for batches of at most 64 tokens
+// and 16 experts (one workgroup per token), or from route_f32_kernel.
+// Routing on gfx950: one wavefront routes one token. Lane l owns experts
 // l, l+64, l+128, l+192; each of the k rounds is a 64-lane max-reduction of
 // 64-bit keys (value key << 32 | ~expert) through cross-lane shuffles.
 // The renormalised weight of slot j is exp(L_j - L_0) / sum_i exp(L_i - L_0),
@@ -217,6 +220,71 @@ __global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
   }
 }
 
+// bf16 router for small batches (decode): one workgroup of 256 threads per
+// token, so the batch's loads spread over as many CUs as it has tokens
+// instead of one CU per 16 tokens. Thread i takes 16-byte column chunks
+// i, i + 256, ... of x and of every router row (EM >= E rows; the rows past
+// E repeat row 0 and their sums are never used), multiplies them in fp32
+// and sums per expert; the 256 partial sums are added in a fixed order
+// (wave shuffles, then the four waves in turn), so the logits are
+// deterministic. J chunks per thread are loaded before the first product:
+// one memory round trip per 2048*J columns.
+template <int EM, int J>
+__global__ __launch_bounds__(256) void route_bf16_narrow_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
+    int T, int d, int E, int k, float* logits, float* probs, int32_t* idx, float* w) {
+  __shared__ float part[4][EM];
+  __shared__ float L[EM];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16_t* xr = x + static_cast<size_t>(t) * d;
+  float acc[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) acc[e] = 0.f;
+  const int nch = d / 8;  // 16-byte chunks per row
+  for (int c0 = tid; c0 < nch; c0 += 256 * J) {
+    uint4 a[J], b[J][EM];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int c = c0 + 256 * j;
+      const int cc = c < nch ? c : 0;
+      a[j] = *reinterpret_cast<const uint4*>(xr + 8 * cc);
+      if (c >= nch) a[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EM; ++e)
+        b[j][e] = *reinterpret_cast<const uint4*>(wr + static_cast<size_t>(e < E ? e : 0) * d + 8 * cc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t av[4] = {a[j].x, a[j].y, a[j].z, a[j].w};
+#pragma unroll
+      for (int e = 0; e < EM; ++e) {
+        const uint32_t bv[4] = {b[j][e].x, b[j][e].y, b[j][e].z, b[j][e].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[e] = fmaf(__uint_as_float(av[q] << 16), __uint_as_float(bv[q] << 16), acc[e]);
+          acc[e] = fmaf(__uint_as_float(av[q] & 0xFFFF0000u), __uint_as_float(bv[q] & 0xFFFF0000u), acc[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    const float s = wave_sum_f32(acc[e]);
+    if (lane == 0) part[wave][e] = s;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  if (lane < EM) {
+    float s = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    if (lane < E && bias) s += bias[lane];
+    L[lane] = s;
+    if (logits && lane < E) logits[static_cast<size_t>(t) * E + lane] = s;
+  }
+  const size_t tE = static_cast<size_t>(t) * E, tk = static_cast<size_t>(t) * k;
+  route_token(L, E, k, probs ? probs + tE : nullptr, idx + tk, w + tk);
+}
+
 // fp32 router: one wave per token, lanes split the width, experts in turn.
 __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x,
                                                         const float* __restrict__ wr,
@@ -244,6 +312,8 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
   route_token(&L[wave][0], E, k, probs ? probs + tE : nullptr, idx + tk, w + tk);
 }
 
+constexpr int kNarrowRouterTokens = 64;
+
 template <int NB, int NW>
 moe_status launch_route_bf16(const void* x, const void* wr, const float* bias, int T, int d, int E,
                              int k, float* logits, float* probs, int32_t* idx, float* w,
@@ -270,6 +340,13 @@ moe_status launch_route(const void* x, const void* w_router, const float* bias, 
     route_f32_kernel<<<(T + 3) / 4, 256, 0, s>>>(static_cast<const float*>(x),
                                                  static_cast<const float*>(w_router), bias, T, d,
                                                  E, k, logits, probs, topk_idx, topk_w);
+    return launch_status();
+  }
+  // up to 64 tokens: one workgroup per token (decode batches)
+  if (T <= kNarrowRouterTokens && E <= 16) {
+    auto kern = E <= 8 ? route_bf16_narrow_kernel<8, 2> : route_bf16_narrow_kernel<16, 2>;
+    kern<<<T, 256, 0, s>>>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router),
+                           bias, T, d, E, k, logits, probs, topk_idx, topk_w);
     return launch_status();
   }
   if (E <= 16) return launch_route_bf16<1, 16>(x, w_router, bias, T, d, E, k, logits, probs, topk_idx, topk_w, s);

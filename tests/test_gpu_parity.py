@@ -90,7 +90,12 @@ def test_permute_bitexact(M, kind, T, E, k):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T,d,E,k,bias", [(64, 64, 4, 2, False), (300, 256, 8, 2, False),
                                           (1000, 2048, 64, 8, True), (31, 4096, 8, 2, False),
-                                          (20, 112, 200, 16, True)])
+                                          (20, 112, 200, 16, True),
+                                          # one workgroup per token (at most 64 tokens and
+                                          # 16 experts): minimal width, widths past one load
+                                          # round, k = E, and the first batch above the limit
+                                          (1, 16, 16, 4, True), (64, 8192, 12, 3, True),
+                                          (33, 2080, 16, 16, False), (65, 512, 8, 2, False)])
 def test_route_fused(M, dtype, T, d, E, k, bias):
     say(f"moe_route dtype={dtype} T={T} d={d} E={E} k={k} bias={bias}")
     inp = wl.make_custom_inputs(T, d, 16, E, dtype, seed=3, bias=bias)
