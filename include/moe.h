@@ -57,9 +57,8 @@
  *     shapes (the 16-bit expert outputs dominate there). Narrower layers
  *     with one term reached 4e-2 x RMS, which is why they take two.
  *   - Precision, MOE_F32: fp32 throughout (within 1e-4 x RMS of the exact
- *     layer). The fp32 expert kernels are a small-shape parity path: one
- *     thread per output element and no tiling; they are not meant for
- *     large layers.
+ *     layer): the expert GEMMs run on the fp32 MFMA (fp32 products and
+ *     accumulation) in 128 x 128 tiles, SiLU with IEEE expf and division.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

@@ -924,42 +924,151 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: one thread per output element, plain fp32 FMA loops. Only for
-// the fp32 dtype (small parity workloads); grid = (rows, column blocks).
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E, int r) {
-  int lo = 0, hi = E;  // largest e with offsets[e] <= r
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= r) lo = mid; else hi = mid;
-  }
-  return lo;
-}
+// fp32 path: the same grouped GEMMs on the fp32 MFMA (v_mfma_f32_32x32x2_f32,
+// fp32 products and accumulation). 128 x 128 tiles (gate/up: 64 gate rows
+// and the same 64 up rows, giving 64 columns of h; down: 128 columns of y),
+// scheduled by the same device-side tile map as the bf16 kernels (one
+// split part: y is a single fp32 partial). Four waves, each 64 token rows x
+// 64 weight rows: 2 x 2 accumulators of 32 x 32. The reduction moves in
+// steps of 16 through two LDS stages filled from registers (each thread
+// loads 16 bytes of two A rows and two B rows per step, stored after the
+// step's MFMAs); LDS rows are 16 floats padded to 20, so the 16-byte
+// fragment reads of 16 lanes (16 rows, 80 bytes apart) touch 64 distinct
+// banks. In the MFMA for sub-step s, lane l supplies reduction index
+// 8*(l/32) + s of its row (for both operands), so each lane reads its 8
+// values of a step with two 16-byte reads.
+constexpr int TMF = 128;           // token rows and weight rows per fp32 tile
+constexpr int TKF = 16;            // reduction step (fp32 elements)
+constexpr int LDF = TKF + 4;       // LDS row stride (floats)
+typedef float f32x16f __attribute__((ext_vector_type(16)));
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void expert_gemm_f32_kernel(
     const float* __restrict__ A, const int32_t* __restrict__ sorted_token,
     const int32_t* __restrict__ offsets, int E, const float* __restrict__ B0,
-    const float* __restrict__ B1, int N, int K, float* __restrict__ C,
+    const float* __restrict__ B1, int N, int K, float* __restrict__ C, int n_cu,
     int32_t* __restrict__ split_out) {
-  const int r = blockIdx.x;
-  const int n = blockIdx.y * 256 + threadIdx.x;
-  if (!GATE_UP && split_out && r == 0 && n == 0) *split_out = 1;
-  if (r >= offsets[E] || n >= N) return;
-  const int e = expert_of_row(offsets, E, r);
-  const float* a = A + static_cast<size_t>(GATE_UP ? sorted_token[r] : r) * K;
-  const float* b0 = B0 + (static_cast<size_t>(e) * N + n) * K;
-  if (GATE_UP) {
-    const float* b1 = B1 + (static_cast<size_t>(e) * N + n) * K;
-    float g = 0.f, u = 0.f;
-    for (int i = 0; i < K; ++i) {
-      g = fmaf(a[i], b0[i], g);
-      u = fmaf(a[i], b1[i], u);
+  __shared__ __attribute__((aligned(16))) float sa[2][TMF * LDF];
+  __shared__ __attribute__((aligned(16))) float sb[2][TMF * LDF];
+  __shared__ int s_map[kMapLdsInts];
+  const int nN = GATE_UP ? (N + 63) / 64 : (N + TMF - 1) / TMF;
+  const int nk = K / TKF;  // K is a multiple of 16
+  Tile tile;
+  const bool have = map_tile<TMF>(offsets, E, nN, 1, n_cu, nk, 0, GATE_UP ? 2 * N : N, &tile, s_map);
+  if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = 1;
+  if (!have) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  // weight rows of the tile: gate/up rows 0-63 are gate rows n0 .. n0+63,
+  // rows 64-127 the same rows of up; down rows are n0 + r
+  const int n0 = GATE_UP ? tile.nt * 64 : tile.nt * TMF;
+  const size_t wexp = static_cast<size_t>(tile.e) * N * K;
+  // loads: thread t moves 16 bytes (4 floats, chunk t % 4) of rows t/4 and
+  // t/4 + 64 of each operand per step
+  const int lr = tid >> 2, lc = (tid & 3) * 4;
+  const float* ap[2];
+  const float* bp[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = lr + 64 * h;
+    const int rr = r < tile.rows ? r : r % tile.rows;  // past the rows: repeat a valid one
+    const size_t arow = GATE_UP ? static_cast<size_t>(sorted_token[tile.row0 + rr])
+                                : static_cast<size_t>(tile.row0 + rr);
+    ap[h] = A + arow * K + lc;
+    const int n = min(n0 + (GATE_UP ? (r & 63) : r), N - 1);
+    bp[h] = ((GATE_UP && r >= 64) ? B1 : B0) + wexp + static_cast<size_t>(n) * K + lc;
+  }
+  float4 ra[2], rb[2];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = *reinterpret_cast<const float4*>(ap[h] + kt * TKF);
+      rb[h] = *reinterpret_cast<const float4*>(bp[h] + kt * TKF);
     }
-    C[static_cast<size_t>(r) * N + n] = silu(g) * u;
-  } else {
-    float s = 0.f;
-    for (int i = 0; i < K; ++i) s = fmaf(a[i], b0[i], s);
-    C[static_cast<size_t>(r) * N + n] = s;
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<float4*>(&sa[st][(lr + 64 * h) * LDF + lc]) = ra[h];
+      *reinterpret_cast<float4*>(&sb[st][(lr + 64 * h) * LDF + lc]) = rb[h];
+    }
+  };
+  // fragments: token block mb of the wave is tile rows wm*64 + 32 mb + l%32;
+  // weight block nb: gate/up nb = 0 gate rows wn*32 + l%32, nb = 1 the same
+  // rows of up (tile rows 64 + ...); down rows wn*64 + 32 nb + l%32
+  const int kh = (lane >> 5) * 8;
+  int fa[2], fb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    fa[i] = (wm * 64 + 32 * i + (lane & 31)) * LDF + kh;
+    const int brow = GATE_UP ? 64 * i + wn * 32 + (lane & 31) : wn * 64 + 32 * i + (lane & 31);
+    fb[i] = brow * LDF + kh;
+  }
+  f32x16f acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  gload(0);
+  lstore(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    __syncthreads();  // stage st written; stage st ^ 1 no longer read
+    if (kt + 1 < nk) gload(kt + 1);
+    float4 wa[2][2], tb[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        wa[i][q] = *reinterpret_cast<const float4*>(&sb[st][fb[i] + 4 * q]);
+        tb[i][q] = *reinterpret_cast<const float4*>(&sa[st][fa[i] + 4 * q]);
+      }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const int q = s8 >> 2, c = s8 & 3;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[nb][q][c], tb[mb][q][c],
+                                                            acc[nb][mb], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(st ^ 1);
+  }
+
+  // acc[nb][mb] element i: token row wm*64 + 32 mb + l%32, weight-tile row
+  // (block nb) + 8*(i/4) + 4*(l/32) + i%4: four consecutive columns per group
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = wm * 64 + 32 * mb + (lane & 31);
+    if (m >= tile.rows) continue;
+    float* crow = C + static_cast<size_t>(tile.row0 + m) * N;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j = 8 * g + 4 * (lane >> 5);
+      if (GATE_UP) {
+        const int n = n0 + wn * 32 + j;
+        if (n < N)
+          *reinterpret_cast<float4*>(crow + n) =
+              make_float4(silu(acc[0][mb][4 * g]) * acc[1][mb][4 * g],
+                          silu(acc[0][mb][4 * g + 1]) * acc[1][mb][4 * g + 1],
+                          silu(acc[0][mb][4 * g + 2]) * acc[1][mb][4 * g + 2],
+                          silu(acc[0][mb][4 * g + 3]) * acc[1][mb][4 * g + 3]);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int n = n0 + wn * 64 + 32 * nb + j;
+          if (n < N)
+            *reinterpret_cast<float4*>(crow + n) =
+                make_float4(acc[nb][mb][4 * g], acc[nb][mb][4 * g + 1], acc[nb][mb][4 * g + 2],
+                            acc[nb][mb][4 * g + 3]);
+        }
+      }
+    }
   }
 }
 
@@ -1023,9 +1132,9 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
   const int rows = T * k;
   if (sp && !stream_self_permute(rows, E, dt)) return MOE_UNSUPPORTED;
   if (dt == MOE_F32) {
-    expert_gemm_f32_kernel<true><<<dim3(rows, (ffn + 255) / 256), 256, 0, s>>>(
+    expert_gemm_f32_kernel<true><<<tile_grid(rows, E, TMF, (ffn + 63) / 64, 1), 256, 0, s>>>(
         static_cast<const float*>(x), sorted_token, offsets, E, static_cast<const float*>(w_gate),
-        static_cast<const float*>(w_up), ffn, d, static_cast<float*>(h), nullptr);
+        static_cast<const float*>(w_up), ffn, d, static_cast<float*>(h), cu_count(), nullptr);
     return launch_status();
   }
   bf16_t* hl = static_cast<bf16_t*>(h_lo);
@@ -1060,9 +1169,9 @@ moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, 
                        hipStream_t s) {
   const int rows = T * k;
   if (dt == MOE_F32) {
-    expert_gemm_f32_kernel<false><<<dim3(rows, (d + 255) / 256), 256, 0, s>>>(
+    expert_gemm_f32_kernel<false><<<tile_grid(rows, E, TMF, (d + TMF - 1) / TMF, 1), 256, 0, s>>>(
         static_cast<const float*>(h), nullptr, offsets, E, static_cast<const float*>(w_down),
-        nullptr, d, ffn, static_cast<float*>(y), split);
+        nullptr, d, ffn, static_cast<float*>(y), cu_count(), split);
     return launch_status();
   }
   const bf16_t* hb = static_cast<const bf16_t*>(h);

@@ -128,6 +128,11 @@ def test_route_fused(M, dtype, T, d, E, k, bias):
 EXPERT_SHAPES = [
     # T, d, ffn, E, k, dtype, routing kind
     (64, 64, 128, 4, 2, "f32", "random"),
+    # fp32 MFMA tiles (128 x 128): several row and column tiles with ragged
+    # ends in both passes, long reductions, empty and light experts
+    (700, 272, 336, 5, 2, "f32", "random"),
+    (300, 1040, 2064, 3, 2, "f32", "one_heavy"),
+    (50, 128, 64, 8, 1, "f32", "even_only"),
     (300, 256, 320, 8, 2, "bf16", "random"),
     (257, 272, 336, 8, 2, "bf16", "random"),      # ragged K and N tails
     (200, 128, 192, 8, 3, "bf16", "all_same"),    # experts 3..7 empty
