@@ -11,8 +11,9 @@
 // bf16 MFMA), from route_bf16_narrow_kernel for batches of at most 64 tokens
 // and 16 experts (one workgroup per token), or from route_f32_kernel.
 // Routing on gfx950: one wavefront routes one token. Lane l owns experts
-// l, l+64, l+128, l+192; each of the k rounds is a 64-lane max-reduction of
-// 64-bit keys (value key << 32 | ~expert) through cross-lane shuffles.
+// l, l+64, l+128, l+192; each of the k rounds takes the largest order key
+// left (a 64-lane maximum on the VALU's data-parallel moves) and, among the
+// experts holding it, the lowest index (a ballot).
 // The renormalised weight of slot j is exp(L_j - L_0) / sum_i exp(L_i - L_0),
 // which equals p_j / sum_i p_i because the softmax denominator cancels.
 #include "common.h"
@@ -26,19 +27,26 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, kWave);
-  uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, kWave);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
+// Largest of the 64 lanes' values, in every lane: row shifts by 1, 2, 4 and
+// 8 leave each 16-lane row's maximum in its lane 15, two row broadcasts
+// carry it to lane 63 (all on the VALU's data-parallel moves, no LDS), and
+// lane 63 is read out. Lanes a move has no source for keep their value,
+// which leaves a maximum unchanged.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto mx = [](uint32_t a, int b) { return a > static_cast<uint32_t>(b) ? a : static_cast<uint32_t>(b); };
+  const int iv = static_cast<int>(v);
+  v = mx(v, __builtin_amdgcn_update_dpp(iv, iv, 0x111, 0xf, 0xf, false));  // row_shr:1
+  int t = static_cast<int>(v);
+  v = mx(v, __builtin_amdgcn_update_dpp(t, t, 0x112, 0xf, 0xf, false));   // row_shr:2
+  t = static_cast<int>(v);
+  v = mx(v, __builtin_amdgcn_update_dpp(t, t, 0x114, 0xf, 0xf, false));   // row_shr:4
+  t = static_cast<int>(v);
+  v = mx(v, __builtin_amdgcn_update_dpp(t, t, 0x118, 0xf, 0xf, false));   // row_shr:8
+  t = static_cast<int>(v);
+  v = mx(v, __builtin_amdgcn_update_dpp(t, t, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  t = static_cast<int>(v);
+  v = mx(v, __builtin_amdgcn_update_dpp(t, t, 0x143, 0xc, 0xf, false));   // row_bcast:31
+  return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -59,45 +67,43 @@ __device__ void route_token(const float* Lrow, int E, int k, float* probs_row,
                             int32_t* idx_row, float* w_row) {
   const int lane = threadIdx.x & (kWave - 1);
   float v[4];
-  uint64_t key[4];
+  uint32_t kv[4];  // order keys; 0 (below every finite value's key) past E
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + q * kWave;
     v[q] = e < E ? Lrow[e] : -INFINITY;
-    key[q] = e < E ? ((static_cast<uint64_t>(order_key(v[q])) << 32) | static_cast<uint32_t>(~e)) : 0ull;
+    kv[q] = e < E ? order_key(v[q]) : 0u;
   }
+  // k rounds: the largest order key among the experts not yet taken (a
+  // wave maximum over each lane's largest untaken key), then the lowest
+  // expert holding that key (a ballot per key slot, q = 0 first: lane l,
+  // slot q is expert l + 64q); it takes slot j and drops out. Order keys
+  // of finite values are at least 0x007FFFFF, so 0 marks "no expert".
   int my_e = 0;
-  float my_v = 0.f, v0;
-  if (E <= kWave) {
-    // One key per lane. Lane l's slot is the rank of its key (how many of the
-    // E keys are larger; keys are distinct, so the ranks are 0 .. E-1; lanes
-    // past E hold key 0 and rank E >= k). The keys are read out lane by lane
-    // on the scalar path, then each selected lane hands its expert and logit
-    // to the lane of its slot.
-    const uint32_t khi = static_cast<uint32_t>(key[0] >> 32), klo = static_cast<uint32_t>(key[0]);
-    int rank = 0;
-    for (int m = 0; m < E; ++m) {
-      const uint32_t mhi = __builtin_amdgcn_readlane(khi, m), mlo = __builtin_amdgcn_readlane(klo, m);
-      rank += (mhi > khi || (mhi == khi && mlo > klo)) ? 1 : 0;
+  float my_v = 0.f, v0 = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t best = kv[0];
+    if (E > kWave) {
+#pragma unroll
+      for (int q = 1; q < 4; ++q) best = kv[q] > best ? kv[q] : best;
     }
-    my_e = __builtin_amdgcn_ds_permute(rank * 4, lane);
-    my_v = __int_as_float(__builtin_amdgcn_ds_permute(rank * 4, __float_as_int(v[0])));
-    v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
-  } else {
-    // k rounds of a 64-lane maximum over four keys per lane
-    v0 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
+    const uint32_t m = wave_max_u32(best);
+    int e = -1;
 #pragma unroll
-      for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
-      best = wave_max_u64(best);
-      const int e = static_cast<int>(~static_cast<uint32_t>(best));
-      const float ve = Lrow[e];
-      if (j == 0) v0 = ve;
-      if (lane == j) { my_e = e; my_v = ve; }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lane + q * kWave == e) key[q] = 0ull;
+    for (int q = 0; q < 4; ++q) {
+      if (q > 0 && E <= kWave) break;
+      const uint64_t b = __ballot(kv[q] == m);
+      if (e < 0 && b != 0) {
+        const int l = static_cast<int>(__builtin_ctzll(b));
+        e = l + q * kWave;
+        if (lane == l) kv[q] = 0u;
+      }
+    }
+    const float ve = Lrow[e < 0 ? 0 : e];  // (e >= 0: m is some lane's key)
+    if (j == 0) v0 = ve;
+    if (lane == j) {
+      my_e = e;
+      my_v = ve;
     }
   }
   if (probs_row) {
