@@ -291,7 +291,12 @@ __global__ __launch_bounds__(256) void route_bf16_narrow_kernel(
   route_token(L, E, k, probs ? probs + tE : nullptr, idx + tk, w + tk);
 }
 
-// fp32 router: one wave per token, lanes split the width, experts in turn.
+// fp32 router: one wave per token (four per workgroup). Experts go in
+// chunks of EC: each lane keeps EC partial sums over its columns (float4
+// chunks 4l, 4l + 256, ... of x and of the EC router rows), so x is read
+// once per chunk and the experts' loads go out together; then EC wave sums
+// in a fixed order. Rows past E repeat row E-1 and are never stored.
+template <int EC>
 __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x,
                                                         const float* __restrict__ wr,
                                                         const float* __restrict__ bias, int T, int d,
@@ -302,13 +307,30 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
   const int t = blockIdx.x * 4 + wave;
   const bool valid = t < T;
   const float* xr = x + static_cast<size_t>(valid ? t : 0) * d;
-  for (int e = 0; e < E && valid; ++e) {
-    const float* wrow = wr + static_cast<size_t>(e) * d;
-    float s = 0.f;
-    for (int i = lane; i < d; i += kWave) s = fmaf(xr[i], wrow[i], s);
-    s = wave_sum_f32(s);
-    if (bias) s += bias[e];
-    if (lane == 0) L[wave][e] = s;
+  for (int e0 = 0; e0 < E && valid; e0 += EC) {
+    float acc[EC];
+#pragma unroll
+    for (int j = 0; j < EC; ++j) acc[j] = 0.f;
+    for (int c = 4 * lane; c < d; c += 4 * kWave) {
+      const float4 xv = *reinterpret_cast<const float4*>(xr + c);
+#pragma unroll
+      for (int j = 0; j < EC; ++j) {
+        const int e = min(e0 + j, E - 1);
+        const float4 wv = *reinterpret_cast<const float4*>(wr + static_cast<size_t>(e) * d + c);
+        acc[j] = fmaf(xv.x, wv.x, acc[j]);
+        acc[j] = fmaf(xv.y, wv.y, acc[j]);
+        acc[j] = fmaf(xv.z, wv.z, acc[j]);
+        acc[j] = fmaf(xv.w, wv.w, acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < EC; ++j) {
+      float s = wave_sum_f32(acc[j]);
+      if (lane == 0 && e0 + j < E) {
+        if (bias) s += bias[e0 + j];
+        L[wave][e0 + j] = s;
+      }
+    }
   }
   __syncthreads();
   if (!valid) return;
@@ -343,9 +365,10 @@ moe_status launch_route(const void* x, const void* w_router, const float* bias, 
                         int E, int k, moe_dtype dt, float* logits, float* probs,
                         int32_t* topk_idx, float* topk_w, hipStream_t s) {
   if (dt == MOE_F32) {
-    route_f32_kernel<<<(T + 3) / 4, 256, 0, s>>>(static_cast<const float*>(x),
-                                                 static_cast<const float*>(w_router), bias, T, d,
-                                                 E, k, logits, probs, topk_idx, topk_w);
+    auto kern = E <= 4 ? route_f32_kernel<4> : (E <= 8 ? route_f32_kernel<8> : route_f32_kernel<16>);
+    kern<<<(T + 3) / 4, 256, 0, s>>>(static_cast<const float*>(x),
+                                     static_cast<const float*>(w_router), bias, T, d, E, k, logits,
+                                     probs, topk_idx, topk_w);
     return launch_status();
   }
   // up to 64 tokens: one workgroup per token (decode batches)
