@@ -172,7 +172,9 @@ int main() {
     if (check<256, false>(off, E, rows_bound, nN, 1, n_cu, nk, &tiles, 64)) return 1;
     // the down pass with h in two bf16 terms: 128 output rows per tile
     if (check<128, false>(off, E, rows_bound, nN, max_split, n_cu, nk, &tiles)) return 1;
-    cases += 4;
+    // the fp32 kernels: 128-row tiles, one split part, either order per expert
+    if (check<128, false>(off, E, rows_bound, nN, 1, n_cu, nk, &tiles, 0, wrows)) return 1;
+    cases += 5;
   }
   printf("ok: %d cases, %lld tiles\n", cases, tiles);
   return 0;
