@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA (fp32 layers)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE layer tokens/sec + % bf16 MFMA peak (active FLOPs), d4096/ffn14336/E8/top2"
 CPU_SAMPLE = {"tiny": 64, "small": 2048, "prefill": 4096, "decode": 32, "skewed": 8192}
@@ -45,6 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {  # the files whose text defines each dominant kernel
     "expert_gemm_bf16_kernel": ["expert_gemm.hip", "common.h"],
     "expert_stream_kernel": ["expert_stream.hip", "common.h"],
+    "expert_gemm_f32_kernel": ["expert_gemm.hip", "common.h"],
 }
 
 
@@ -235,9 +237,12 @@ def main():
 
 def gate_up_kernel(w, rows):
     """Name and family of the gate/up kernel the library launches for this
-    shape (its own switches: weight streaming for at most 32 rows per expert
-    on average, 384-row tiles from 768, 256-row tiles between)."""
+    shape (its own switches: fp32 layers on the fp32 MFMA tiles; bf16 layers
+    weight streaming for at most 32 rows per expert on average, 384-row tiles
+    from 768, 256-row tiles between)."""
     kmask = "true" if w.d % 64 else "false"
+    if w.dtype == "f32":
+        return "expert_gemm_f32_kernel<true>", "expert_gemm_f32_kernel", "mfma"
     if rows <= 32 * w.E:
         nb = 1 if rows <= 16 * w.E else 2
         # bf16 batches of at most 256 assignments derive their permutation
@@ -299,8 +304,9 @@ def measure_layer(moe, w, dv, steps, warmup):
     gu_s = stage_ms["gate_up"] / 1e3
     kname, family, bound = gate_up_kernel(w, rows)
     if bound == "mfma":
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         roof = {"kernel": kname, "bound": "mfma", "achieved": gu_flops / gu_s / 1e12,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+                "peak": peak, "unit": "TFLOP/s"}
     else:
         roof = {"kernel": kname, "bound": "hbm", "achieved": gu_bytes / gu_s / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
