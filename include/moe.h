@@ -193,7 +193,7 @@ moe_status moe_forward_profiled(const void* x, const void* w_router, const void*
  * Limit: shapes whose moe_workspace_size(T, d, ffn, E, k, dt) exceeds
  * MOE_NO_ALLOC_SCRATCH_BYTES return MOE_WORKSPACE_TOO_SMALL and enqueue
  * nothing (at the Mixtral widths d = 4096, ffn = 14336, E = 8, k = 2 that
- * is T above 431 tokens: decode-sized batches fit). The first call on a
+ * is T above 430 tokens: decode-sized batches fit). The first call on a
  * device looks up that device's copy of the array (MOE_HIP_ERROR if the
  * lookup fails). Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race and give undefined

@@ -8,9 +8,11 @@
 // fp32, which fixes the rounding independently of scheduling.
 //
 // y holds S partial sums of the down GEMM's reduction (S is read from the
-// device, where the down GEMM chose it), fp32 for an fp32 layer and in the
-// 24-bit format of common.h for a bf16 layer; each expert row is the sum of
-// its S parts in part order, then weighted. Each thread owns 8 consecutive
+// device, where the down GEMM chose it; S = 0 means the count is given per
+// row and 256-column tile in a part table, where the 384-row down tiles
+// record one part, or two for an XCD's tail tiles), fp32 for an fp32 layer
+// and in the 24-bit format of common.h for a bf16 layer; each expert row is
+// the sum of its parts in part order, then weighted. Each thread owns 8 consecutive
 // columns of one token (32 or 24 bytes per term); a workgroup covers 2048
 // columns.
 //
@@ -86,6 +88,7 @@ struct CombineExtra {
   size_t ys_stride;         // elements between parts
   int n_shared, T;
   const void* resid;        // residual input [T, d] (fp32 or bf16), or null
+  const uint8_t* parts;     // partial sums per (y row, 256-column tile) when *split == 0
 };
 
 // RES: 0 no residual, 1 fp32 residual, 2 bf16 residual; SH: shared experts;
@@ -96,11 +99,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       size_t split_stride,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int d, int k,
-                                                      CombineExtra ex, OT* __restrict__ out) {
+                                                      CombineExtra ex, const uint8_t* __restrict__ parts,
+                                                      OT* __restrict__ out) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (col >= d) return;
+  // S partial sums for every row, or (S = 0) the count of each row's
+  // 256-column tile in parts
   const int S = *split;
+  const int nct = (d + 255) / 256, ct = col >> 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const int p = inv_pos[static_cast<size_t>(t) * k + j];
@@ -109,7 +116,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     const size_t at = static_cast<size_t>(p) * d + col;
     float v[8];
     load_y<F24>(y, at, v);
-    for (int s = 1; s < S; ++s) {
+    const int Sp = S > 0 ? S : parts[static_cast<size_t>(p) * nct + ct];
+    for (int s = 1; s < Sp; ++s) {
       float u[8];
       load_y<F24>(y, at + s * split_stride, u);
 #pragma unroll
@@ -151,7 +159,7 @@ void combine_launch(dim3 grid, hipStream_t s, const void* y, const int32_t* spli
                     const int32_t* inv_pos, const float* w, int d, int k, const CombineExtra& ex,
                     void* out) {
   combine_kernel<OT, RES, SH, F24><<<grid, 256, 0, s>>>(y, split, stride, inv_pos, w, d, k, ex,
-                                                        static_cast<OT*>(out));
+                                                        ex.parts, static_cast<OT*>(out));
 }
 
 template <typename OT, bool F24>
@@ -177,10 +185,10 @@ moe_status launch_combine_ext(const void* y, const int32_t* split, const int32_t
                               const float* topk_w, int T, int d, int k, moe_dtype dt,
                               const void* ys, const int32_t* ys_split, int n_shared,
                               const void* resid, moe_dtype resid_dt, void* out, moe_dtype out_dt,
-                              hipStream_t s) {
+                              hipStream_t s, const uint8_t* y_parts) {
   dim3 grid(T, (d + 2047) / 2048);
   const size_t stride = static_cast<size_t>(T) * k * d;
-  CombineExtra ex{ys, ys_split, static_cast<size_t>(T) * n_shared * d, n_shared, T, resid};
+  CombineExtra ex{ys, ys_split, static_cast<size_t>(T) * n_shared * d, n_shared, T, resid, y_parts};
   const int res = resid == nullptr ? 0 : (resid_dt == MOE_F32 ? 1 : 2);
   const bool f24 = dt == MOE_BF16;
   if (out_dt == MOE_F32) {
@@ -195,9 +203,9 @@ moe_status launch_combine_ext(const void* y, const int32_t* split, const int32_t
 
 moe_status launch_combine(const void* y, const int32_t* split, const int32_t* inv_pos,
                           const float* topk_w, int T, int d, int k, moe_dtype dt, void* out,
-                          moe_dtype out_dt, hipStream_t s) {
+                          moe_dtype out_dt, hipStream_t s, const uint8_t* y_parts) {
   return launch_combine_ext(y, split, inv_pos, topk_w, T, d, k, dt, nullptr, nullptr, 0, nullptr,
-                            MOE_F32, out, out_dt, s);
+                            MOE_F32, out, out_dt, s, y_parts);
 }
 
 }  // namespace moe

@@ -134,7 +134,8 @@ struct Workspace {
   void* h;                // [T*k, ffn] in dt
   void* h_lo;             // [T*k, ffn] bf16: second term of h (two_term_h), else null
   void* y;                // [down_split_bound(ffn), T*k, d] partial sums of the down GEMM (y_bytes(dt) each)
-  int32_t* split;         // [1] number of partial sums in y
+  int32_t* split;         // [1] number of partial sums in y; 0: per (row, column tile) in y_parts
+  uint8_t* y_parts;       // [T*k, ceil(d/256)] partial sums of each row's 256-column tile (split = 0)
   int32_t* block_counts;  // [kPermMaxBlocks * E] per-block expert histograms of the permutation
   size_t bytes;
 };
@@ -158,6 +159,7 @@ inline Workspace carve_workspace(void* base, int T, int d, int ffn, int E, int k
   w.h_lo = two_term_h(d, ffn, dt) ? take(tk * static_cast<size_t>(ffn) * es) : nullptr;
   w.y = take(down_split_bound(ffn) * tk * static_cast<size_t>(d) * y_bytes(dt));
   w.split = reinterpret_cast<int32_t*>(take(4));
+  w.y_parts = reinterpret_cast<uint8_t*>(take(tk * static_cast<size_t>((d + 255) / 256)));
   w.block_counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(kPermMaxBlocks) * E * 4));
   w.bytes = off;
   return w;
@@ -253,7 +255,7 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
                           const StreamPermute* sp = nullptr);
 moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
                        int T, int d, int ffn, int E, int k, moe_dtype dt, void* y, int32_t* split,
-                       hipStream_t s);
+                       hipStream_t s, uint8_t* y_parts = nullptr);
 // Weight-streaming kernels; experts with more than max_rows rows are skipped
 // (left to a tiled launch). The down pass cuts its reduction into at most
 // max_split parts.
@@ -273,12 +275,13 @@ moe_status launch_router_stats(const float* probs, const int32_t* counts, int T,
 // y (and ys) in the format of a layer of dtype dt: 24-bit for bf16, fp32.
 moe_status launch_combine(const void* y, const int32_t* split, const int32_t* inv_pos,
                           const float* topk_w, int T, int d, int k, moe_dtype dt, void* out,
-                          moe_dtype out_dt, hipStream_t s);
+                          moe_dtype out_dt, hipStream_t s, const uint8_t* y_parts = nullptr);
 // ys: outputs of n_shared shared experts (their own split count ys_split);
 // resid: [T, d] in resid_dt added last; both optional.
 moe_status launch_combine_ext(const void* y, const int32_t* split, const int32_t* inv_pos,
                               const float* topk_w, int T, int d, int k, moe_dtype dt, const void* ys,
                               const int32_t* ys_split, int n_shared, const void* resid,
-                              moe_dtype resid_dt, void* out, moe_dtype out_dt, hipStream_t s);
+                              moe_dtype resid_dt, void* out, moe_dtype out_dt, hipStream_t s,
+                              const uint8_t* y_parts = nullptr);
 
 }  // namespace moe

@@ -623,7 +623,14 @@ void expert_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restr
 // cost is coarser row padding, so the host takes these tiles only when the
 // experts average at least two tiles' worth of rows. The tiles of an XCD's
 // last, at most half-full round run at half width (384 x 128, 96 x 64 per
-// wave; see assign_tile's TAIL). Same swizzle, stages and epilogue as the
+// wave; see assign_tile's TAIL), except in a down pass given a part table:
+// there every tile keeps its whole reduction and those tail tiles run at
+// full width with their reduction in two halves (two partial sums; the
+// table tells the combine which rows and 256-column tiles have two), which
+// keeps the tail's bytes per FLOP and saves a tile boundary per CU and the
+// second partial sum of the other tiles against a uniform split in two
+// (prefill down pass 791 -> 767 us, combine 52 -> 41 us). Same swizzle,
+// stages and epilogue as the
 // 256 x 256 kernel. Which operand and
 // which weight matrix each load instruction serves is fixed per unrolled
 // index, so the compiler keeps the choice in scalar code (chosen at run
@@ -665,7 +672,7 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
                              const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, int N,
                              int K, void* __restrict__ Cv, bf16_t* __restrict__ Clo, int max_split,
                              int n_cu, size_t c_split, int32_t* __restrict__ split_out,
-                             int min_rows) {
+                             int min_rows, uint8_t* __restrict__ parts) {
   __shared__ __attribute__((aligned(1024))) char lds0a[STAGE_A3];
   __shared__ __attribute__((aligned(1024))) char lds0b[STAGE];
   __shared__ __attribute__((aligned(1024))) char lds1a[STAGE_A3];
@@ -679,8 +686,20 @@ void expert_gemm_tall_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
   const bool have = map_tile<TM3, true>(offsets, E, nN, max_split, n_cu, nk, min_rows,
                                         GATE_UP ? 2 * N : N, &tile, reinterpret_cast<int*>(lds1a));
   __syncthreads();
-  if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = tile.S;
+  // Down pass with a part table: whole tiles keep their reduction in one
+  // part, and the tail tiles an XCD's last round would run as half-width
+  // tiles run whole-width with their reduction in two halves instead; each
+  // tile records its part count per row in parts.
+  const bool ksplit = !GATE_UP && parts != nullptr;
+  if (!GATE_UP && blockIdx.x == 0 && threadIdx.x == 0) *split_out = ksplit ? 0 : tile.S;
   if (!have) return;
+  if (ksplit && tile.half >= 0) {
+    tile.ks = tile.half;
+    tile.S = 2;
+    tile.half = -1;
+  }
+  if (ksplit && static_cast<int>(threadIdx.x) < tile.rows)
+    parts[static_cast<size_t>(tile.row0 + threadIdx.x) * nN + tile.nt] = static_cast<uint8_t>(tile.S);
   const int kbeg = tile.ks * nk / tile.S, kend = (tile.ks + 1) * nk / tile.S;
 
   const int lane = threadIdx.x & 63;
@@ -1156,7 +1175,7 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
     auto kern = d % TK ? expert_gemm_tall_kernel<true, true> : expert_gemm_tall_kernel<true, false>;
     const int ncu = cu_count();
     kern<<<tall_grid(rows, E, (ffn + 127) / 128, 1, ncu), NW3 * 64, 0, s>>>(
-        xb, sorted_token, offsets, E, wg, wu, ffn, d, h, hl, 1, ncu, 0, nullptr, 0);
+        xb, sorted_token, offsets, E, wg, wu, ffn, d, h, hl, 1, ncu, 0, nullptr, 0, nullptr);
     return launch_status();
   }
   launch_256<true, false>(xb, nullptr, sorted_token, offsets, E, wg, wu, ffn, d, h, hl, rows, 1, 0,
@@ -1166,7 +1185,7 @@ moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int3
 
 moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, const void* w_down,
                        int T, int d, int ffn, int E, int k, moe_dtype dt, void* y, int32_t* split,
-                       hipStream_t s) {
+                       hipStream_t s, uint8_t* y_parts) {
   const int rows = T * k;
   if (dt == MOE_F32) {
     expert_gemm_f32_kernel<false><<<tile_grid(rows, E, TMF, (d + TMF - 1) / TMF, 1), 256, 0, s>>>(
@@ -1203,9 +1222,12 @@ moe_status launch_down(const void* h, const void* h_lo, const int32_t* offsets, 
   if (use_tall_tiles(rows, E)) {
     auto kern = ffn % TK ? expert_gemm_tall_kernel<false, true> : expert_gemm_tall_kernel<false, false>;
     const int ncu = cu_count();
-    kern<<<tall_grid(rows, E, (d + TW - 1) / TW, max_split, ncu), NW3 * 64, 0, s>>>(
-        hb, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, max_split, ncu, c_split,
-        split, 0);
+    // long reductions with a part table: one part per tile, two for the tail tiles
+    const bool ksplit = y_parts != nullptr && max_split >= 2;
+    const int ms = ksplit ? 1 : max_split;
+    kern<<<tall_grid(rows, E, (d + TW - 1) / TW, ms, ncu), NW3 * 64, 0, s>>>(
+        hb, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, ms, ncu, c_split, split, 0,
+        ksplit ? y_parts : nullptr);
     return launch_status();
   }
   launch_256<false, false>(hb, nullptr, nullptr, offsets, E, wd, nullptr, d, ffn, y, nullptr, rows,

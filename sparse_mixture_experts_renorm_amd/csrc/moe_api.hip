@@ -218,10 +218,11 @@ static moe_status run_experts(const void* x, const int32_t* topk_idx, const floa
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[3], stream);
   st = launch_down(ws.h, ws.h_lo, ws.offsets, w_down, T, d, ffn, E, k, dt, ws.y, ws.split,
-                   stream);
+                   stream, ws.y_parts);
   if (st != MOE_OK) return st;
   if (ev) hipEventRecord(ev[4], stream);
-  st = launch_combine(ws.y, ws.split, ws.inv_pos, topk_w, T, d, k, dt, out, out_dt, stream);
+  st = launch_combine(ws.y, ws.split, ws.inv_pos, topk_w, T, d, k, dt, out, out_dt, stream,
+                      ws.y_parts);
   if (ev) hipEventRecord(ev[5], stream);
   return st;
 }
@@ -350,7 +351,8 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
   st = launch_gate_up(xl, b.sorted_token, b.offsets, w_gate, w_up, T, d, ffn, E, k, dt, b.h,
                       b.h_lo, stream);
   if (st != MOE_OK) return st;
-  st = launch_down(b.h, b.h_lo, b.offsets, w_down, T, d, ffn, E, k, dt, b.y, b.split, stream);
+  st = launch_down(b.h, b.h_lo, b.offsets, w_down, T, d, ffn, E, k, dt, b.y, b.split, stream,
+                   b.y_parts);
   if (st != MOE_OK) return st;
   if (S > 0) {
     // shared experts: S more experts that every token reaches, T rows each
@@ -364,7 +366,7 @@ moe_status moe_forward_ext(const void* x, const void* w_router, const void* w_ga
     if (st != MOE_OK) return st;
   }
   return launch_combine_ext(b.y, b.split, b.inv_pos, b.topk_w, T, d, k, dt, w.y_s, w.split_s, S,
-                            opt->residual ? x : nullptr, dt, out, out_dt, stream);
+                            opt->residual ? x : nullptr, dt, out, out_dt, stream, b.y_parts);
 }
 
 moe_status moe_forward_no_alloc(const void* x, const void* w_router, const void* w_gate,

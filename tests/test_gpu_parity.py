@@ -171,6 +171,10 @@ EXPERT_SHAPES = [
     (600, 1040, 1104, 4, 2, "bf16", "random"),   # 256 x 256 tiles
     (2000, 1040, 1040, 2, 1, "bf16", "random"),  # tall tiles
     (1500, 1024, 1024, 2, 2, "bf16", "one_heavy"),  # tall tiles, no tails, one expert empty
+    # tall down tiles with a part table: a reduction long enough to split and
+    # so few tiles that every one runs as two halves (2064 = 32 * 64 + 16:
+    # the second half ends in a tail)
+    (800, 1024, 2064, 2, 2, "bf16", "random"),
 ]
 
 
