@@ -249,6 +249,10 @@ inline bool stream_self_permute(int rows, int E, moe_dtype dt) {
 // h - h_hi (see store_h); the down pass then multiplies both terms.
 // sp: null, or (when stream_self_permute holds) the routing from which the
 // stream kernel derives sorted_token and offsets, which it then writes.
+// y_parts: null, or a part table [T*k, ceil(d/256)] that a 384-row down
+// pass with a long reduction fills (one byte per row and 256-column tile:
+// its count of partial sums), writing 0 to *split; every other down pass
+// writes its uniform count of partial sums to *split.
 moe_status launch_gate_up(const void* x, const int32_t* sorted_token, const int32_t* offsets,
                           const void* w_gate, const void* w_up, int T, int d, int ffn, int E,
                           int k, moe_dtype dt, void* h, void* h_lo, hipStream_t s,
