@@ -122,6 +122,9 @@ CAPACITY = [  # T, d, ffn, E, k, dtype, seed, bias, cf
     (32, 256, 512, 8, 2, "bf16", 6, True, 1.0),      # few rows per expert: streaming kernels
     (2048, 1024, 2816, 8, 2, "bf16", 0, True, 1.0),  # the small workload's shape, skewed
     (3000, 256, 320, 8, 2, "bf16", 20, True, 1.0),   # 6000 assignments: multi-block permutation
+    # 384-row down tiles with a part table, expert 0 losing 645 of its 1260
+    # rows: the dropped rows are in no tile and the combine never reads them
+    (1536, 1024, 1552, 2, 1, "bf16", 32, True, 0.8),
 ]
 
 
