@@ -379,7 +379,7 @@ def _timed(fn, steps, warmup):
 def extras(args, w, moe, wl, dv, lay, call, to_dev, log):
     """Timings of the calls beyond the plain layer (see the module docstring)."""
     import numpy as np
-    steps, warm = max(1, min(args.steps, 10)), max(1, min(args.warmup, 3))
+    steps, warm = max(1, min(args.steps, 20)), max(1, args.warmup)
     out = {}
     _, ex = moe.moe_forward(*lay, **call, want_probs=True, want_counts=True)
     probs, counts = ex["probs"], ex["counts"]
